@@ -1,0 +1,61 @@
+"""Build libattn_fwd.so (gfx950) in-tree with hipcc.
+
+Always recompiles.  The library is written next to this file so that it travels
+with the source tree; nothing is installed elsewhere.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip")]
+LIBRARY = os.path.join(HERE, "libattn_fwd.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # keep the compiler from forming packed-fp32 VALU instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    return "hipcc"
+
+
+def build(verbose=False, resource_report=None):
+    """Compile the HIP sources into LIBRARY; returns its path.
+
+    resource_report: optional path; when given, the compiler's per-kernel register /
+    LDS / occupancy remarks are written there.
+    """
+    fd, tmp = tempfile.mkstemp(prefix=".libattn_fwd.", suffix=".so.tmp", dir=HERE)
+    os.close(fd)
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + SOURCES
+    if resource_report:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if resource_report:
+        with open(resource_report, "w") as f:
+            f.write(res.stdout + res.stderr)
+    if res.returncode != 0:
+        os.unlink(tmp)
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

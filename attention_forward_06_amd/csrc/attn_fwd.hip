@@ -1,0 +1,580 @@
+// Fused scaled-dot-product attention forward for AMD Instinct MI355X (gfx950, CDNA4).
+//
+// One templated kernel covers the three mask modes:
+//   none / causal  -- FlashAttention-2 online softmax over key tiles: running row max m,
+//                     running exp-sum l, fp32 accumulator rescaled by alpha = 2^(m_old - m_new),
+//                     O = acc / l at the end ("Triton-CUDA Attention", online-softmax core and
+//                     full example; "Fused Attention", _attn_fwd_inner / _attn_fwd).  Causal
+//                     runs the tiles left of the query block unmasked and masks only the
+//                     tiles that straddle the diagonal ("Fused Attention", stages 1 and 2).
+//   block_diag     -- one diagonal block per workgroup, a single key tile with an exact
+//                     softmax and no rescaling ("TLX Block Attention", kernel).
+// Exponentials are 2^x (v_exp_f32) with sm_scale * log2(e) folded into one FMA
+// ("Triton-CUDA Attention", online-softmax core).
+//
+// gfx950 mapping (see the layout notes above each helper):
+//   * Each wave owns 32 query rows.  It computes S^T = K_tile * Q^T with
+//     v_mfma_f32_32x32x16_{f16,bf16}: K rows are the A operand (read from LDS), Q^T the
+//     B operand (held in VGPRs for the whole loop).  The 32x32 accumulator then gives each
+//     lane ONE query (lane % 32) and 16 of the tile's keys, so the row max / row sum are
+//     in-lane plus one exchange with lane ^ 32.
+//   * The K row fed to MFMA row rho is key pi(rho) (bits 2 and 3 of rho swapped).  With that
+//     choice the 16 scores a lane holds per 32-key subtile are, per 16-key chunk, exactly the
+//     8 consecutive keys the P.V MFMA wants from that lane -- P never leaves the registers.
+//   * O^T = V^T * P^T: P^T is the B operand (the lane's own probabilities, packed to 16-bit or
+//     fp8), V^T the A operand, read from the row-major V tile in LDS with the gfx950
+//     transposing loads ds_read_b64_tr_b16 / ds_read_b64_tr_b8.  The O^T accumulator keeps
+//     the lane's query too, so alpha and 1/l are per-lane scalars.
+//   * fp8 V: P is rounded to OCP e5m2 (v_cvt_pk_bf8_f32, round-to-nearest-even) and P.V runs
+//     on v_mfma_f32_32x32x64_f8f6f4 with both operands in bf8 (e5m2) format; the row sum uses
+//     the unrounded fp32 P ("Fused Attention", _attn_fwd_inner fp8 branch).
+//   * K/V tiles are staged HBM -> VGPR -> LDS with 128-bit buffer loads (rows past L read as
+//     zero), prefetching tile t+1 while tile t is consumed.
+//   * Workgroup ids are remapped so all query blocks of one (batch, head) land on the same
+//     XCD (its K/V stays in that XCD's L2), heaviest causal blocks first.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/attn_fwd.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((__vector_size__(16)));
+typedef unsigned int u32x2 __attribute__((__vector_size__(8)));
+typedef int i32x8 __attribute__((__vector_size__(32)));
+typedef int i32x2 __attribute__((__vector_size__(8)));
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef _Float16 f16x8 __attribute__((__vector_size__(16)));
+typedef float f32x16 __attribute__((__vector_size__(64)));
+
+constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskBlock = 2;
+constexpr int kF16 = 0, kBF16 = 1, kBF16V8 = 2;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+
+struct Params {
+  const unsigned char* q;
+  const unsigned char* k;
+  const unsigned char* v;
+  unsigned char* o;
+  float* lse;
+  int L;
+  int bh;          // batch * heads
+  int n_qblocks;   // query blocks per (batch, head)
+  float c;         // sm_scale * log2(e)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// 128-bit load; offsets at or past the resource size return zeros.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == kF16) {
+    f16x8 x, y;
+    __builtin_memcpy(&x, &a, 16);
+    __builtin_memcpy(&y, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(x, y, c, 0, 0, 0);
+  } else {
+    bf16x8 x, y;
+    __builtin_memcpy(&x, &a, 16);
+    __builtin_memcpy(&y, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+  }
+}
+
+// Two fp32 -> packed 16-bit (round to nearest even).
+template <int DT>
+__device__ __forceinline__ unsigned pack2(float lo, float hi) {
+  if constexpr (DT == kF16) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    unsigned short ua, ub;
+    __builtin_memcpy(&ua, &a, 2);
+    __builtin_memcpy(&ub, &b, 2);
+    return (unsigned)ua | ((unsigned)ub << 16);
+  } else {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    unsigned short ua, ub;
+    __builtin_memcpy(&ua, &a, 2);
+    __builtin_memcpy(&ub, &b, 2);
+    return (unsigned)ua | ((unsigned)ub << 16);
+  }
+}
+
+// MFMA row rho of the S^T = K * Q^T product reads key pi(rho): bits 2 and 3 swapped.
+__device__ __forceinline__ int key_of_row(int rho) {
+  return (rho & 0x13) | ((rho & 4) << 1) | ((rho >> 1) & 4);
+}
+
+__device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32); }
+
+template <int D, int DT, int MODE, int NW, int BN>
+struct Cfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = 32 * NW;
+  static constexpr int KT = BN / 32;          // 32-key subtiles per tile
+  static constexpr int DK = D / 16;           // 16-wide d chunks of Q.K
+  static constexpr int DTL = D / 32;          // 32-wide d tiles of O
+  static constexpr bool V8 = (DT == kBF16V8);
+  static constexpr int VB = V8 ? 1 : 2;       // bytes per V element
+  static constexpr int KROW = D * 2 + 16;     // LDS bytes per K row (16 B pad)
+  static constexpr int VROW = D * VB + 32;    // LDS bytes per V row (32 B pad)
+  static constexpr int KCH = BN * D * 2 / 16 / NT;   // 16-byte chunks of K per thread
+  static constexpr int VCH = BN * D * VB / 16 / NT;  // 16-byte chunks of V per thread
+  static constexpr int LDS_BYTES = BN * KROW + BN * VROW;
+  static_assert(BN % 32 == 0, "key tile is a whole number of 32-key subtiles");
+  static_assert(!V8 || BN % 64 == 0, "fp8 P.V consumes 64 keys per MFMA");
+  static_assert(BN * D * 2 % (16 * NT) == 0 && BN * D * VB % (16 * NT) == 0,
+                "tile splits evenly into 16-byte chunks per thread");
+  static_assert(D % 32 == 0, "head dim is a multiple of 32");
+};
+
+// Workgroup id -> (batch*head, query block).  Ids are dealt round-robin to the 8 XCDs;
+// the remap gives each XCD a contiguous range of (batch*head, query block) pairs so one
+// head's K/V is shared in one L2.  Causal blocks run last-query-block first (most work).
+__device__ __forceinline__ void block_coords(int id, int total, int nqb, bool heavy_first, int& bh,
+                                             int& qb) {
+  int logical = id;
+  if ((total & 7) == 0) logical = (id & 7) * (total >> 3) + (id >> 3);
+  bh = logical / nqb;
+  qb = logical - bh * nqb;
+  if (heavy_first) qb = nqb - 1 - qb;
+}
+
+template <int D, int DT, int MODE, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
+  using C = Cfg<D, DT, MODE, NW, BN>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* ldsK = smem;
+  unsigned char* ldsV = smem + BN * C::KROW;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;        // which half of the wave (k sub-block of the MFMA operands)
+  const int col = lane & 31;      // the lane's query within the wave's 32
+
+  int bh, qb;
+  block_coords(blockIdx.x, gridDim.x, p.n_qblocks, MODE == kMaskCausal, bh, qb);
+  const int L = p.L;
+  const int m0 = qb * C::BM;              // first query row of the workgroup
+  const int qw0 = m0 + 32 * wave;         // first query row of this wave
+  const int my_q = qw0 + col;
+
+  const size_t head_elems = (size_t)L * D;
+  const unsigned char* qh = p.q + (size_t)bh * head_elems * 2;
+  const unsigned char* kh = p.k + (size_t)bh * head_elems * 2;
+  const unsigned char* vh = p.v + (size_t)bh * head_elems * C::VB;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, (unsigned)(head_elems * 2));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, (unsigned)(head_elems * 2));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, (unsigned)(head_elems * C::VB));
+
+  // Key range walked by this workgroup.
+  int key_begin = 0, key_end = L;
+  if constexpr (MODE == kMaskCausal) key_end = min(L, m0 + C::BM);
+  if constexpr (MODE == kMaskBlock) {
+    key_begin = m0;
+    key_end = m0 + C::BM;
+  }
+  const int ntiles = (key_end - key_begin + BN - 1) / BN;
+
+  // Q^T fragment (B operand): lane holds Q[my_q][16*kk + 8*h .. +7] for every kk.
+  u32x4 qf[C::DK];
+#pragma unroll
+  for (int kk = 0; kk < C::DK; ++kk) {
+    const unsigned off = (unsigned)(my_q < L ? (my_q * D + 16 * kk + 8 * h) * 2 : head_elems * 2);
+    qf[kk] = buf_load16(rq, off);
+  }
+
+  // Global -> register prefetch of one K/V tile; rows at or past L come back as zeros.
+  u32x4 kreg[C::KCH], vreg[C::VCH];
+  auto load_tile = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < C::KCH; ++i) {
+      const int chunk = tid + i * C::NT;
+      const int row = chunk / (D / 8);
+      const int cc = chunk % (D / 8);
+      const int key = key0 + row;
+      const unsigned off = (unsigned)(key < L ? (key * D + cc * 8) * 2 : head_elems * 2);
+      kreg[i] = buf_load16(rk, off);
+    }
+#pragma unroll
+    for (int i = 0; i < C::VCH; ++i) {
+      const int chunk = tid + i * C::NT;
+      constexpr int per_row = D * C::VB / 16;
+      const int row = chunk / per_row;
+      const int cc = chunk % per_row;
+      const int key = key0 + row;
+      const unsigned off =
+          (unsigned)(key < L ? (unsigned)key * D * C::VB + cc * 16 : head_elems * C::VB);
+      vreg[i] = buf_load16(rv, off);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::KCH; ++i) {
+      const int chunk = tid + i * C::NT;
+      const int row = chunk / (D / 8);
+      const int cc = chunk % (D / 8);
+      *(u32x4*)(ldsK + row * C::KROW + cc * 16) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::VCH; ++i) {
+      const int chunk = tid + i * C::NT;
+      constexpr int per_row = D * C::VB / 16;
+      const int row = chunk / per_row;
+      const int cc = chunk % per_row;
+      *(u32x4*)(ldsV + row * C::VROW + cc * 16) = vreg[i];
+    }
+  };
+
+  f32x16 acc[C::DTL];
+#pragma unroll
+  for (int dt = 0; dt < C::DTL; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m_run = -INFINITY;   // running max of scores * c (log2 domain)
+  float l_run = 0.f;         // running sum of 2^(s*c - m_run) over this lane's keys
+
+  // LDS addresses that do not change across tiles.
+  const int krow_lane = key_of_row(col);
+  const unsigned char* kfrag_base = ldsK + krow_lane * C::KROW + h * 16;
+  // ds_read_b64_tr_b16: in each 16-lane group, lane 4e+q supplies the address of row e,
+  // 4-element column block q; the instruction hands lane 4q+c element e of that block.
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr16_row = 8 * (g16 >> 1) + (s16 >> 2);
+  const int tr16_col = 16 * (g16 & 1) + 4 * (s16 & 3);
+  // ds_read_b64_tr_b8: lane 2e+q supplies row e, 8-byte column block q.
+  const int tr8_row = 8 * (g16 >> 1) + (s16 >> 1);
+  const int tr8_col = 16 * (g16 & 1) + 8 * (s16 & 1);
+
+  if (ntiles > 0) load_tile(key_begin);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int key0 = key_begin + t * BN;
+    __syncthreads();   // every wave is done reading the previous tile
+    store_tile();
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(key0 + BN);   // in flight while this tile is consumed
+
+    // Which 32-key subtiles this wave needs, and which need an element mask.
+    bool live[C::KT], masked[C::KT];
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) {
+      const int n0 = key0 + 32 * kt;
+      if constexpr (MODE == kMaskCausal) {
+        live[kt] = n0 <= qw0 + 31;
+        masked[kt] = n0 + 31 > qw0;
+      } else if constexpr (MODE == kMaskNone) {
+        live[kt] = n0 < L;
+        masked[kt] = n0 + 31 >= L;
+      } else {
+        live[kt] = true;
+        masked[kt] = false;
+      }
+    }
+
+    // ---- S^T = K * Q^T ------------------------------------------------------------------
+    f32x16 s[C::KT];
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+      if (live[kt]) {
+        const unsigned char* kb = kfrag_base + 32 * kt * C::KROW;
+#pragma unroll
+        for (int kk = 0; kk < C::DK; ++kk) {
+          const u32x4 a = *(const u32x4*)(kb + kk * 32);
+          s[kt] = mfma_qk<DT>(a, qf[kk], s[kt]);
+        }
+      }
+    }
+
+    // ---- mask, row max ------------------------------------------------------------------
+    // Lane's register r of subtile kt holds key key0 + 32*kt + 16*(r/8) + 8*h + r%8.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) {
+      if (!live[kt]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = -INFINITY;
+        continue;
+      }
+      if (masked[kt]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kt + 16 * (r >> 3) + 8 * h + (r & 7);
+          bool ok;
+          if constexpr (MODE == kMaskCausal) ok = key <= my_q;
+          else ok = key < L;
+          if (!ok) s[kt][r] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    }
+    mx = xor32_max(mx);
+
+    // ---- online softmax update ------------------------------------------------------------
+    const float m_new = fmaxf(m_run, mx * p.c);
+    const float neg = -m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], p.c, neg));
+        s[kt][r] = e;
+        psum += e;
+      }
+    if constexpr (MODE == kMaskBlock) {
+      l_run = psum;   // single tile: nothing to rescale
+    } else {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < C::DTL; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
+    m_run = m_new;
+
+    // ---- O^T += V^T * P^T -----------------------------------------------------------------
+    if constexpr (!C::V8) {
+#pragma unroll
+      for (int cc = 0; cc < BN / 16; ++cc) {
+        const int kt = cc >> 1, c8 = (cc & 1) * 8;
+        if (!live[kt]) continue;
+        u32x4 pb;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pb[w] = pack2<DT>(s[kt][c8 + 2 * w], s[kt][c8 + 2 * w + 1]);
+#pragma unroll
+        for (int dt = 0; dt < C::DTL; ++dt) {
+          const unsigned char* vb =
+              ldsV + (16 * cc + tr16_row) * C::VROW + (32 * dt + tr16_col) * 2;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vb));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vb + 4 * C::VROW));
+          u32x4 a;
+          __builtin_memcpy(&a, &lo, 8);
+          __builtin_memcpy((char*)&a + 8, &hi, 8);
+          acc[dt] = mfma_qk<DT>(a, pb, acc[dt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u64 = 0; u64 < BN / 64; ++u64) {
+        if (!live[2 * u64] && !live[2 * u64 + 1]) continue;
+        // P bytes: byte 16*u + r <- subtile 2*u64+u, register r (key 16*(2u + r/8) + 8h + r%8).
+        i32x8 pb;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int u = w >> 2, r = (w & 3) * 4;
+          int word = __builtin_amdgcn_cvt_pk_bf8_f32(s[2 * u64 + u][r], s[2 * u64 + u][r + 1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_bf8_f32(s[2 * u64 + u][r + 2], s[2 * u64 + u][r + 3], word, true);
+          pb[w] = word;
+        }
+#pragma unroll
+        for (int dt = 0; dt < C::DTL; ++dt) {
+          i32x8 a;
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4) {
+            const unsigned char* vb =
+                ldsV + (64 * u64 + 16 * t4 + tr8_row) * C::VROW + 32 * dt + tr8_col;
+            const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) i32x2*)(vb));
+            a[2 * t4] = x[0];
+            a[2 * t4 + 1] = x[1];
+          }
+          acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, acc[dt], 1, 1, 0, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: O = acc / l, rounded to Q's type; optional natural-log normaliser -------
+  const float l_tot = xor32_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (my_q < L) {
+    unsigned char* orow = p.o + ((size_t)bh * head_elems + (size_t)my_q * D) * 2;
+#pragma unroll
+    for (int dt = 0; dt < C::DTL; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        // registers 4*a4 .. 4*a4+3 hold d = 32*dt + 8*a4 + 4*h + 0..3
+        u32x2 w;
+        w[0] = pack2<DT == kF16 ? kF16 : kBF16>(acc[dt][4 * a4] * inv, acc[dt][4 * a4 + 1] * inv);
+        w[1] = pack2<DT == kF16 ? kF16 : kBF16>(acc[dt][4 * a4 + 2] * inv, acc[dt][4 * a4 + 3] * inv);
+        *(u32x2*)(orow + (32 * dt + 8 * a4 + 4 * h) * 2) = w;
+      }
+    if (p.lse != nullptr && h == 0)
+      p.lse[(size_t)bh * L + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Host side: validation, instance table, launch.
+// ------------------------------------------------------------------------------------------
+
+template <int D, int DT, int MODE, int NW, int BN>
+hipError_t launch(const Params& p0, hipStream_t stream) {
+  using C = Cfg<D, DT, MODE, NW, BN>;
+  Params p = p0;
+  p.n_qblocks = (p.L + C::BM - 1) / C::BM;
+  const long long blocks = (long long)p.n_qblocks * p.bh;
+  auto kern = attn_fwd_kernel<D, DT, MODE, NW, BN>;
+  if (C::LDS_BYTES > 64 * 1024) {
+    static bool raised = false;   // per instance; the attribute is process-wide
+    if (!raised) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::NT), C::LDS_BYTES, stream, p);
+  return hipGetLastError();
+}
+
+struct Problem {
+  int64_t batch, heads, L, D;
+  float sm_scale;
+  int mode;
+  int64_t block_size;
+  int dtype;
+};
+
+bool supported(const Problem& pr) {
+  const bool dense = pr.mode == kMaskNone || pr.mode == kMaskCausal;
+  if (dense) {
+    if (pr.D == 64 || pr.D == 128) return pr.dtype == kF16 || pr.dtype == kBF16;
+    if (pr.D == 256) return true;
+    return false;
+  }
+  if (pr.D != 64 && pr.D != 128) return false;
+  if (pr.dtype != kF16 && pr.dtype != kBF16) return false;
+  return pr.block_size == 32 || pr.block_size == 64 || pr.block_size == 128;
+}
+
+attn_status_t validate(const Problem& pr) {
+  if (pr.mode < 0 || pr.mode > 2 || pr.dtype < 0 || pr.dtype > 2) return ATTN_ERR_ARG;
+  if (!std::isfinite(pr.sm_scale) || !(pr.sm_scale > 0.f)) return ATTN_ERR_ARG;
+  if (pr.batch < 0 || pr.heads < 0 || pr.L < 0 || pr.D <= 0) return ATTN_ERR_SHAPE;
+  if (pr.mode == kMaskBlock) {
+    if (pr.block_size <= 0) return ATTN_ERR_SHAPE;
+    if (pr.L % pr.block_size != 0) return ATTN_ERR_SHAPE;
+  }
+  // Sizes: every count must fit the kernel's index types.
+  const int64_t lim = (int64_t)1 << 31;
+  if (pr.L >= lim || pr.batch >= lim || pr.heads >= lim) return ATTN_ERR_SHAPE;
+  if (pr.batch > 0 && pr.heads > (INT64_MAX / pr.batch)) return ATTN_ERR_SHAPE;
+  const int64_t bh = pr.batch * pr.heads;
+  if (bh >= lim) return ATTN_ERR_SHAPE;
+  if (pr.L > 0 && pr.D > INT64_MAX / 2 / pr.L) return ATTN_ERR_SHAPE;
+  if (pr.L * pr.D * 2 >= lim) return ATTN_ERR_SHAPE;            // one head must fit 2^31 bytes
+  if (bh > 0 && pr.L * pr.D > INT64_MAX / 2 / bh) return ATTN_ERR_SHAPE;
+  if (((pr.L + 31) / 32) * bh >= lim) return ATTN_ERR_SHAPE;    // workgroup count fits the grid
+  if (!supported(pr)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+template <int D, int DT>
+hipError_t dispatch_dense(int mode, const Params& p, hipStream_t s) {
+  if (mode == kMaskCausal) return launch<D, DT, kMaskCausal, 4, 64>(p, s);
+  return launch<D, DT, kMaskNone, 4, 64>(p, s);
+}
+
+template <int D, int DT>
+hipError_t dispatch_block(int64_t bs, const Params& p, hipStream_t s) {
+  if (bs == 32) return launch<D, DT, kMaskBlock, 1, 32>(p, s);
+  if (bs == 64) return launch<D, DT, kMaskBlock, 2, 64>(p, s);
+  return launch<D, DT, kMaskBlock, 4, 128>(p, s);
+}
+
+hipError_t dispatch(const Problem& pr, const Params& p, hipStream_t s) {
+  if (pr.mode == kMaskBlock) {
+    if (pr.D == 64) return pr.dtype == kF16 ? dispatch_block<64, kF16>(pr.block_size, p, s)
+                                            : dispatch_block<64, kBF16>(pr.block_size, p, s);
+    return pr.dtype == kF16 ? dispatch_block<128, kF16>(pr.block_size, p, s)
+                            : dispatch_block<128, kBF16>(pr.block_size, p, s);
+  }
+  switch (pr.D) {
+    case 64:
+      return pr.dtype == kF16 ? dispatch_dense<64, kF16>(pr.mode, p, s)
+                              : dispatch_dense<64, kBF16>(pr.mode, p, s);
+    case 128:
+      return pr.dtype == kF16 ? dispatch_dense<128, kF16>(pr.mode, p, s)
+                              : dispatch_dense<128, kBF16>(pr.mode, p, s);
+    default:
+      if (pr.dtype == kF16) return dispatch_dense<256, kF16>(pr.mode, p, s);
+      if (pr.dtype == kBF16) return dispatch_dense<256, kBF16>(pr.mode, p, s);
+      return dispatch_dense<256, kBF16V8>(pr.mode, p, s);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_check(int64_t batch, int64_t heads, int64_t L, int64_t D, float sm_scale,
+                             attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype) {
+  Problem pr{batch, heads, L, D, sm_scale, (int)mask_mode, block_size, (int)dtype};
+  return validate(pr);
+}
+
+attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t batch, int64_t heads, int64_t L, int64_t D, float sm_scale,
+                           attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype,
+                           void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  Problem pr{batch, heads, L, D, sm_scale, (int)mask_mode, block_size, (int)dtype};
+  const attn_status_t st = validate(pr);
+  if (st != ATTN_OK) return st;
+  if (batch * heads * L == 0) return ATTN_OK;
+  Params p{};
+  p.q = (const unsigned char*)q;
+  p.k = (const unsigned char*)k;
+  p.v = (const unsigned char*)v;
+  p.o = (unsigned char*)o;
+  p.lse = lse;
+  p.L = (int)L;
+  p.bh = (int)(batch * heads);
+  p.c = sm_scale * kLog2e;
+  const hipError_t e = dispatch(pr, p, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t batch,
+                       int64_t heads, int64_t L, int64_t D, float sm_scale, attn_mask_t mask_mode,
+                       int64_t block_size, attn_dtype_t dtype, void* stream) {
+  return attn_fwd_lse(q, k, v, o, nullptr, batch, heads, L, D, sm_scale, mask_mode, block_size,
+                      dtype, stream);
+}
+
+const char* attn_status_str(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer argument";
+    case ATTN_ERR_SHAPE: return "invalid shape (negative size, overflow, or block_size not dividing L)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported (mask mode, head dim, dtype, block size) combination";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    case ATTN_ERR_ARG: return "invalid scalar argument (enum value or sm_scale)";
+  }
+  return "unknown status";
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

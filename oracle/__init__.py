@@ -22,12 +22,12 @@ Parity status: every function here is pinned by tests/test_oracle.py against
 brute force, a library routine, closed forms or invariants, except where its
 docstring says "parity unpinned".
 """
-from .attention import (MODES, visible_mask, attn_weights, attn_ref, attn_online_ref,
+from .attention import (MODES, visible_mask, attn_weights, attn_ref, attn_online_ref, attn_lse_ref,
                         visible_pairs, attn_flops)
-from .brute import attn_brute
+from .brute import attn_brute, lse_brute
 from .fp_formats import (round_e5m2, round_bf16, round_f16, e5m2_decode, e5m2_encode,
                          round_to_format)
 
-__all__ = ["MODES", "visible_mask", "attn_weights", "attn_ref", "attn_online_ref",
-           "visible_pairs", "attn_flops", "attn_brute", "round_e5m2", "round_bf16",
+__all__ = ["MODES", "visible_mask", "attn_weights", "attn_ref", "attn_online_ref", "attn_lse_ref",
+           "visible_pairs", "attn_flops", "attn_brute", "lse_brute", "round_e5m2", "round_bf16",
            "round_f16", "e5m2_decode", "e5m2_encode", "round_to_format"]

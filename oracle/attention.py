@@ -137,6 +137,26 @@ def attn_ref(q, k, v, mode, sm_scale, block_size=0, rows=None, p_round=None, chu
     return out
 
 
+def attn_lse_ref(q, k, mode, sm_scale, block_size=0, rows=None):
+    """Natural-log row normaliser lse_i = m_i + ln(sum_j visible exp(S[i, j] - m_i)).
+
+    The fused-attention page stores this per row for a backward pass ([FA-A, _attn_fwd]
+    epilogue: m_i += log(l_i)).  q, k: [B, H, L, D]; returns fp64 [B, H, R].
+    """
+    q, k = _as_f64(q), _as_f64(k)
+    B, H, L, D = q.shape
+    _check_mode(mode, L, block_size)
+    rows = np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((B, H, rows.size), dtype=np.float64)
+    vis = visible_mask(mode, L, block_size, rows)
+    for b in range(B):
+        for h in range(H):
+            S = np.where(vis, sm_scale * (q[b, h][rows] @ k[b, h].T), -np.inf)
+            m = S.max(axis=1)
+            out[b, h] = m + np.log(np.where(vis, np.exp(S - m[:, None]), 0.0).sum(axis=1))
+    return out
+
+
 def attn_online_ref(q, k, v, mode, sm_scale, block_n, block_size=0, rows=None, p_round=None):
     """The pages' online-softmax recurrence in fp64, key tiles of width block_n.
 

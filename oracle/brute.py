@@ -30,3 +30,15 @@ def attn_brute(q, k, v, mode, sm_scale, block_size=0):
         denom = math.fsum(w.values())
         out.append([math.fsum(w[j] * v[j][d] for j in keys) / denom for d in range(D)])
     return out
+
+
+def lse_brute(q, k, mode, sm_scale, block_size=0):
+    """ln(sum_j visible exp(S[i, j])) per row with math.log / math.fsum; [L] floats."""
+    L = len(q)
+    out = []
+    for i in range(L):
+        s = [sm_scale * math.fsum(q[i][d] * k[j][d] for d in range(len(q[i])))
+             for j in range(L) if _visible(mode, i, j, block_size)]
+        top = max(s)
+        out.append(top + math.log(math.fsum(math.exp(x - top) for x in s)))
+    return out

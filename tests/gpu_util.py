@@ -1,0 +1,33 @@
+"""Helpers shared by the GPU tests (no attention arithmetic here)."""
+import numpy as np
+import torch
+
+from attention_forward_06_amd import binding
+from attention_forward_06_amd.inputs import make_qkv
+
+# Max-abs-error tolerances by storage dtype (fp16, bf16, fp8 V/P).
+TOL = {"f16": 2e-3, "bf16": 1e-2, "bf16_v_e5m2": 5e-2}
+
+
+def to_f64(t):
+    """Exact conversion of a (GPU) tensor to a float64 numpy array."""
+    return t.detach().to(torch.float32).cpu().to(torch.float64).numpy()
+
+
+def gpu_qkv(B, H, L, D, dtype, seed=42, std=1.0, gen_device="cpu"):
+    q, k, v = make_qkv(B, H, L, D, dtype, seed=seed, std=std, device=gen_device)
+    return q.cuda(), k.cuda(), v.cuda()
+
+
+def run(q, k, v, mode, block_size=0, sm_scale=None, lse=False):
+    out = binding.attn_fwd(q, k, v, mask=mode, block_size=block_size, sm_scale=sm_scale,
+                           return_lse=lse)
+    torch.cuda.synchronize()
+    return out
+
+
+def sample_rows(L, n_edge=64, n_rand=64, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(n_edge, L))) | set(range(max(0, L - n_edge), L))
+    rows |= set(rng.integers(0, L, size=min(n_rand, L)).tolist())
+    return np.array(sorted(rows), dtype=np.int64)

@@ -1,0 +1,131 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every function
+include/attn_fwd.h declares, and rejects every bad argument before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_forward_06_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+
+NONE, CAUSAL, BLOCK = 0, 1, 2
+F16, BF16, V8 = 0, 1, 2
+FAKE = 0x1000   # never dereferenced: every call below fails validation or is a no-op
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared_functions() == ["attn_abi_version", "attn_fwd", "attn_fwd_check",
+                                     "attn_fwd_lse", "attn_status_str"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert lib.attn_abi_version() == 1
+    with open(HEADER) as f:
+        assert "#define ATTN_ABI_VERSION 1" in f.read()
+    seen = set()
+    for code in range(6):
+        s = binding.status_str(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 6
+    assert binding.status_str(99) == "unknown status"
+
+
+def _call(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, H=1, L=64, D=128, scale=0.1,
+          mode=NONE, bs=0, dt=F16):
+    return lib.attn_fwd(q, k, v, o, B, H, L, D, scale, mode, bs, dt, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_null_pointers(lib, which):
+    kw = {which: None}
+    assert _call(lib, **kw) == binding.Status.ERR_NULL
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(B=-1), binding.Status.ERR_SHAPE),
+    (dict(H=-3), binding.Status.ERR_SHAPE),
+    (dict(L=-64), binding.Status.ERR_SHAPE),
+    (dict(D=0), binding.Status.ERR_SHAPE),
+    (dict(D=-128), binding.Status.ERR_SHAPE),
+    (dict(mode=BLOCK, bs=0), binding.Status.ERR_SHAPE),
+    (dict(mode=BLOCK, bs=-64), binding.Status.ERR_SHAPE),
+    (dict(mode=BLOCK, L=100, bs=64), binding.Status.ERR_SHAPE),
+    (dict(L=1 << 24, D=128), binding.Status.ERR_SHAPE),           # one head > 2^31 bytes
+    (dict(B=1 << 40, H=1 << 40), binding.Status.ERR_SHAPE),       # product overflows
+    (dict(B=1 << 20, H=1 << 12, L=64), binding.Status.ERR_SHAPE), # batch*heads >= 2^31
+    (dict(D=96), binding.Status.ERR_UNSUPPORTED),
+    (dict(D=32), binding.Status.ERR_UNSUPPORTED),
+    (dict(D=512), binding.Status.ERR_UNSUPPORTED),
+    (dict(D=64, dt=V8), binding.Status.ERR_UNSUPPORTED),
+    (dict(D=128, dt=V8), binding.Status.ERR_UNSUPPORTED),
+    (dict(mode=BLOCK, bs=256, L=512), binding.Status.ERR_UNSUPPORTED),
+    (dict(mode=BLOCK, bs=16, L=64), binding.Status.ERR_UNSUPPORTED),
+    (dict(mode=BLOCK, bs=64, D=256, dt=BF16), binding.Status.ERR_UNSUPPORTED),
+    (dict(mode=BLOCK, bs=64, dt=V8), binding.Status.ERR_UNSUPPORTED),
+    (dict(mode=3), binding.Status.ERR_ARG),
+    (dict(mode=-1), binding.Status.ERR_ARG),
+    (dict(dt=3), binding.Status.ERR_ARG),
+    (dict(scale=float("nan")), binding.Status.ERR_ARG),
+    (dict(scale=float("inf")), binding.Status.ERR_ARG),
+    (dict(scale=0.0), binding.Status.ERR_ARG),
+    (dict(scale=-0.5), binding.Status.ERR_ARG),
+])
+def test_rejected_before_launch(lib, args, code):
+    assert _call(lib, **args) == code
+    # attn_fwd_check reports the same status with no pointers at all
+    a = dict(B=1, H=1, L=64, D=128, scale=0.1, mode=NONE, bs=0, dt=F16)
+    a.update(args)
+    assert lib.attn_fwd_check(a["B"], a["H"], a["L"], a["D"], a["scale"], a["mode"], a["bs"],
+                              a["dt"]) == code
+
+
+@pytest.mark.parametrize("args", [dict(B=0), dict(H=0), dict(L=0), dict(B=0, H=0, L=0),
+                                  dict(mode=BLOCK, bs=64, L=0)])
+def test_empty_problem_is_a_noop(lib, args):
+    # nothing to compute: returns OK without touching the (fake) pointers or the GPU
+    assert _call(lib, **args) == binding.Status.OK
+
+
+@pytest.mark.parametrize("mode,D,dt,bs", [
+    (NONE, 64, F16, 0), (NONE, 128, BF16, 0), (CAUSAL, 64, BF16, 0), (CAUSAL, 128, F16, 0),
+    (NONE, 256, F16, 0), (CAUSAL, 256, BF16, 0), (CAUSAL, 256, V8, 0), (NONE, 256, V8, 0),
+    (BLOCK, 128, F16, 64), (BLOCK, 128, BF16, 128), (BLOCK, 64, F16, 32), (BLOCK, 64, BF16, 128),
+])
+def test_supported_set(lib, mode, D, dt, bs):
+    L = 256
+    assert lib.attn_fwd_check(2, 3, L, D, 0.125, mode, bs, dt) == binding.Status.OK
+    # none / causal accept a ragged L
+    if mode != BLOCK:
+        assert lib.attn_fwd_check(2, 3, 257, D, 0.125, mode, bs, dt) == binding.Status.OK
+        assert lib.attn_fwd_check(2, 3, 1, D, 0.125, mode, bs, dt) == binding.Status.OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        binding.attn_fwd(x, x, x)
+    with pytest.raises(ValueError):
+        binding.attn_fwd(x, x, x, mask="sliding")

@@ -219,6 +219,20 @@ def test_online_rounding_uses_running_max_frame():
     assert abs(o[0, 0, 1, 0] - (9.0 + 8 * 18.0) / 9.0) <= 1e-12
 
 
+# ---------------------------------------------------------------- row normaliser (LSE)
+@pytest.mark.parametrize("mode,bs", [("none", 0), ("causal", 0), ("block_diag", 4)])
+def test_lse_brute_and_closed_form(mode, bs):
+    q, k, _ = _qkv(1, 2, 16, 8, seed=12, scale=2.0)
+    got = oracle.attn_lse_ref(q, k, mode, 0.6, bs)
+    for h in range(2):
+        ref = oracle.lse_brute(q[0, h].tolist(), k[0, h].tolist(), mode, 0.6, bs)
+        assert np.abs(got[0, h] - np.array(ref)).max() <= 1e-12
+    # Q = 0: every visible score is 0, so lse_i = ln(number of visible keys)
+    z = oracle.attn_lse_ref(np.zeros_like(q), k, mode, 0.6, bs)
+    counts = oracle.visible_mask(mode, 16, bs).sum(axis=1)
+    assert np.abs(z[0, 0] - np.log(counts)).max() <= 1e-15
+
+
 # ---------------------------------------------------------------- P10 narrow formats
 def test_p10_e5m2_decode_all_codes():
     codes = np.arange(256, dtype=np.uint8)

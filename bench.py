@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X attention forward (one JSON line on stdout).
+
+A step is one attn_fwd call on the headline workload -- causal attention,
+batch 4, 32 heads, L 4096, head dim 128, bf16 -- with Q, K, V already resident
+in HBM.  `value` is its throughput in algorithmic TFLOP/s (4*D FLOPs per visible
+(query, key) pair).  The same run also times the block-diagonal workload at
+scale (batch 8, 32 heads, N 16384, D 128, fp16, block 64 and 128) in GB/s of
+algorithmic traffic (Q, K, V read once, O written once) against the HBM peak,
+and the two remaining workloads for context.
+
+The oracle (fp64 numpy on the host cores) is timed on a bounded sample of the
+headline workload as `cpu_baseline`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+HEADLINE = "causal_b4_h32_l4096_d128_bf16"
+KERNEL_SOURCE = os.path.join(ROOT, "attention_forward_06_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (e.g. under a profiler)")
+    ap.add_argument("--only", default=None, help="time only this workload name")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(name):
+    """HBM bytes per launch measured by counters, if they were taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != source_digest():
+        return None
+    w = t.get("workloads", {}).get(name)
+    if not w:
+        return None
+    return w.get("hbm_bytes_per_launch")
+
+
+def time_workload(name, steps, warmup):
+    import torch
+    from attention_forward_06_amd import binding
+    from attention_forward_06_amd.inputs import WORKLOADS, make_qkv, default_scale
+    import oracle
+
+    w = WORKLOADS[name]
+    B, H, L, D = w["B"], w["H"], w["L"], w["D"]
+    q, k, v = make_qkv(B, H, L, D, w["dtype"], seed=42, device="cuda")
+    o = torch.empty_like(q)
+    scale = default_scale(D)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, L, D, scale, w["mode"],
+            w["block_size"], w["dtype"], sptr)
+    for _ in range(warmup):
+        st = binding.attn_fwd_raw(*args)
+        if st != 0:
+            raise RuntimeError(f"{name}: {binding.status_str(st)}")
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        binding.attn_fwd_raw(*args)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    # per-launch spread from a second, individually bracketed pass
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(steps, 20))]
+    for a, b in evs:
+        a.record(stream)
+        binding.attn_fwd_raw(*args)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    flops = oracle.attn_flops(w["mode"], B, H, L, D, w["block_size"])
+    vb = 1 if w["dtype"] == "bf16_v_e5m2" else 2
+    nbytes = B * H * L * D * (2 + 2 + vb + 2)
+    ms = total_ms / steps
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return dict(name=name, ms=ms, wall_s=wall, min_ms=per[0], median_ms=per[len(per) // 2],
+                flops=flops, bytes=nbytes, tflops=flops / (ms * 1e-3) / 1e12,
+                gbs=nbytes / (ms * 1e-3) / 1e9, mode=w["mode"], dtype=w["dtype"],
+                shape=dict(B=B, H=H, L=L, D=D, block_size=w["block_size"]))
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+
+
+def cpu_baseline(target_s):
+    """The oracle as it stands, on the host cores, over whole heads of the headline workload."""
+    import numpy as np
+    import oracle
+    from attention_forward_06_amd.inputs import WORKLOADS, make_qkv, default_scale
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    w = WORKLOADS[HEADLINE]
+    L, D = w["L"], w["D"]
+    # one (batch, head) at a time, same distribution and dtype as the GPU inputs
+    heads = 0
+    flops = 0
+    elapsed = 0.0
+    while elapsed < target_s and heads < w["B"] * w["H"]:
+        q, k, v = make_qkv(1, 1, L, D, w["dtype"], seed=1000 + heads)
+        qn, kn, vn = (t.float().double().numpy() for t in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.attn_ref(qn, kn, vn, w["mode"], default_scale(D))
+        elapsed += time.perf_counter() - t0
+        flops += oracle.attn_flops(w["mode"], 1, 1, L, D)
+        heads += 1
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} whole (batch, head) slices of {HEADLINE} (L={L}, D={D}, causal), "
+                      f"fp64 numpy, {elapsed:.1f} s; affinity cores "
+                      f"{len(os.sched_getaffinity(0))}, os.cpu_count {os.cpu_count()}"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported by this build "
+              "(the attention forward is measured on one MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from attention_forward_06_amd import binding
+    binding.load_library()
+
+    if a.copy_calibration:
+        copy_calibration()
+    names = [HEADLINE, "blockdiag_b8_h32_n16384_d128_bs64_f16",
+             "blockdiag_b8_h32_n16384_d128_bs128_f16", "dense_b4_h16_l2048_d64_f16",
+             "causal_b1_h16_l32768_d256_bf16_ve5m2"]
+    if a.only:
+        names = [a.only]
+    res = {}
+    for n in names:
+        steps = a.steps if n != "causal_b1_h16_l32768_d256_bf16_ve5m2" else max(1, a.steps // 10)
+        res[n] = time_workload(n, steps, min(a.warmup, steps))
+        print(f"# {n}: {res[n]['ms']:.4f} ms/launch  {res[n]['tflops']:.1f} TFLOP/s  "
+              f"{res[n]['gbs']:.1f} GB/s", file=sys.stderr, flush=True)
+
+    head = res.get(HEADLINE) or next(iter(res.values()))
+    traffic = load_traffic(head["name"])
+    line = {
+        "metric": "attn fwd TFLOP/s + % MFMA peak (causal L=4096); block-diag GB/s % HBM peak",
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(head["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head["name"], "mask": head["mode"], **head["shape"],
+                   "inputs": "seeded N(0,1), resident in HBM"},
+        "roofline": {"bound": "mfma", "achieved": round(head["tflops"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(head["tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    bd = {}
+    for n, r in res.items():
+        if r["mode"] == "block_diag":
+            bd[f"bs{r['shape']['block_size']}"] = {
+                "workload": n, "GB_per_s": round(r["gbs"], 1), "peak_GB_per_s": PEAK_HBM_GBS,
+                "frac": round(r["gbs"] / PEAK_HBM_GBS, 4), "ms": round(r["ms"], 5),
+                "traffic": load_traffic(n)}
+    if bd:
+        line["block_diag"] = bd
+    others = {}
+    for n, r in res.items():
+        if r["mode"] != "block_diag" and n != head["name"]:
+            peak = PEAK_BF16_TFLOPS
+            others[n] = {"TFLOP_per_s": round(r["tflops"], 2), "frac_bf16_peak": round(r["tflops"] / peak, 4),
+                         "ms": round(r["ms"], 5)}
+    if others:
+        line["other_workloads"] = others
+    line["launch_spread_ms"] = {"min": round(head["min_ms"], 5), "median": round(head["median_ms"], 5)}
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

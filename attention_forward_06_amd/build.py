@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     "-shared",
     # keep the compiler from forming packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code never produces NaN (masked scores are -inf, weights exp2(-inf) = 0), so
+    # max/min need no NaN-quieting canonicalisation
+    "-Xarch_device", "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -93,22 +93,15 @@ __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
-// Two fp32 -> packed 16-bit (round to nearest even).
+// Two fp32 -> packed 16-bit (round to nearest even): one v_cvt_pk_{bf16,f16}_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 template <int DT>
 __device__ __forceinline__ unsigned pack2(float lo, float hi) {
-  if constexpr (DT == kF16) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    unsigned short ua, ub;
-    __builtin_memcpy(&ua, &a, 2);
-    __builtin_memcpy(&ub, &b, 2);
-    return (unsigned)ua | ((unsigned)ub << 16);
-  } else {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    unsigned short ua, ub;
-    __builtin_memcpy(&ua, &a, 2);
-    __builtin_memcpy(&ub, &b, 2);
-    return (unsigned)ua | ((unsigned)ub << 16);
-  }
+  const f32x2 v = {lo, hi};
+  if constexpr (DT == kF16) return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
+  else return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
 // MFMA row rho of the S^T = K * Q^T product reads key pi(rho): bits 2 and 3 swapped.
@@ -128,17 +121,44 @@ struct Cfg {
   static constexpr int DTL = D / 32;          // 32-wide d tiles of O
   static constexpr bool V8 = (DT == kBF16V8);
   static constexpr int VB = V8 ? 1 : 2;       // bytes per V element
-  static constexpr int KROW = D * 2 + 16;     // LDS bytes per K row (16 B pad)
-  static constexpr int VROW = D * VB + 32;    // LDS bytes per V row (32 B pad)
-  static constexpr int KCH = BN * D * 2 / 16 / NT;   // 16-byte chunks of K per thread
-  static constexpr int VCH = BN * D * VB / 16 / NT;  // 16-byte chunks of V per thread
-  static constexpr int LDS_BYTES = BN * KROW + BN * VROW;
+  static constexpr int KROWB = D * 2;         // bytes per K row in LDS (no padding: XOR swizzle)
+  static constexpr int VROWB = D * VB;        // bytes per V row in LDS
+  static constexpr int KTILE = BN * KROWB;
+  static constexpr int VTILE = BN * VROWB;
+  static constexpr int NBUF = MODE == kMaskBlock ? 1 : 2;   // double-buffer the streamed tiles
+  static constexpr int LDS_BYTES = NBUF * (KTILE + VTILE);
+  static constexpr int KDMA = KTILE / 1024 / NW;  // 1 KiB LDS-DMA instructions per wave per K tile
+  static constexpr int VDMA = VTILE / 1024 / NW;
+  // The accumulator is rescaled when a row max grows by more than 2^TAU over the reference
+  // it was accumulated against.  TAU = 0 is the pages' recurrence (every increase rescales,
+  // so the current maximum always has weight exactly 1); a wave skips the rescale only when
+  // no row of it saw a larger maximum.  (A positive TAU trades exactness of the dominant
+  // weight, which bf16 P then rounds, for fewer rescales.)
+  static constexpr float TAU = 0.f;
+  static constexpr int WAVES_PER_EU = (D >= 256) ? 1 : 2;
   static_assert(BN % 32 == 0, "key tile is a whole number of 32-key subtiles");
   static_assert(!V8 || BN % 64 == 0, "fp8 P.V consumes 64 keys per MFMA");
-  static_assert(BN * D * 2 % (16 * NT) == 0 && BN * D * VB % (16 * NT) == 0,
-                "tile splits evenly into 16-byte chunks per thread");
+  static_assert(KTILE % (1024 * NW) == 0 && VTILE % (1024 * NW) == 0,
+                "tiles split into whole 1 KiB DMA instructions per wave");
   static_assert(D % 32 == 0, "head dim is a multiple of 32");
 };
+
+// XOR swizzles of the 16-byte chunks inside a tile row (LDS-DMA writes rows unpadded).
+// K: the 16 lanes of a ds_read_b128 read the same chunk of 16 different rows -> spread rows
+//    over 16 distinct chunk positions of a 256-byte bank window.
+// V (16-bit): a ds_read_b64_tr_b16 half-wave reads 4 rows x 64 contiguous bytes -> give the
+//    4 rows disjoint 64-byte slots.   V (fp8): tr_b8 reads 8 rows x 32 bytes -> 8 slots of 32.
+template <int ROWB>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (ROWB == 128) return (r >> 1) & 7;
+  else return r & 15;
+}
+template <int ROWB, bool V8>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (V8) return 2 * (r & 7);
+  else if constexpr (ROWB == 128) return 4 * ((r >> 1) & 1);
+  else return 4 * (r & 3);
+}
 
 // Workgroup id -> (batch*head, query block).  Ids are dealt round-robin to the 8 XCDs;
 // the remap gives each XCD a contiguous range of (batch*head, query block) pairs so one
@@ -152,16 +172,33 @@ __device__ __forceinline__ void block_coords(int id, int total, int nqb, bool he
   if (heavy_first) qb = nqb - 1 - qb;
 }
 
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
+
+// Value of the lane 32 places away (lanes l and l^32 hold the two halves of one query row).
+__device__ __forceinline__ float partner(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  // r[0]: lanes 32..63 received lanes 0..31; r[1]: lanes 0..31 received lanes 32..63
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 template <int D, int DT, int MODE, int NW, int BN>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(Cfg<D, DT, MODE, NW, BN>::WAVES_PER_EU)))
+void attn_fwd_kernel(Params p) {
   using C = Cfg<D, DT, MODE, NW, BN>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* ldsK = smem;
-  unsigned char* ldsV = smem + BN * C::KROW;
+  // One statically sized LDS array per tile buffer, so the compiler can tell the buffer being
+  // read from the one the DMA is filling (it then does not wait for that DMA before reading).
+  __shared__ __attribute__((aligned(1024))) unsigned char lk0[C::KTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lv0[C::VTILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lk1[C::NBUF == 2 ? C::KTILE : 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char lv1[C::NBUF == 2 ? C::VTILE : 1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int h = lane >> 5;        // which half of the wave (k sub-block of the MFMA operands)
   const int col = lane & 31;      // the lane's query within the wave's 32
 
@@ -179,6 +216,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, (unsigned)(head_elems * 2));
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, (unsigned)(head_elems * 2));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, (unsigned)(head_elems * C::VB));
+  const unsigned k_oob = (unsigned)(head_elems * 2), v_oob = (unsigned)(head_elems * C::VB);
 
   // Key range walked by this workgroup.
   int key_begin = 0, key_end = L;
@@ -189,6 +227,37 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
   }
   const int ntiles = (key_end - key_begin + BN - 1) / BN;
 
+  // HBM -> LDS by DMA: instruction j of a tile fills LDS bytes [1024 j, 1024 j + 1024); lane l
+  // lands at +16 l.  The lane fetches the global chunk that the swizzle stores at that slot;
+  // rows at or past L read as zeros.
+  auto issue_tile = [&](int key0, unsigned char* kb, unsigned char* vb) {
+#pragma unroll
+    for (int i = 0; i < C::KDMA; ++i) {
+      const int j = wave + i * NW;
+      const int byte = j * 1024 + lane * 16;
+      const int row = byte / C::KROWB;
+      const int pos = (byte % C::KROWB) >> 4;
+      const int key = key0 + row;
+      const unsigned off = key < L ? (unsigned)(key * C::KROWB + ((pos ^ swz_k<C::KROWB>(row)) << 4)) : k_oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(kb + j * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::VDMA; ++i) {
+      const int j = wave + i * NW;
+      const int byte = j * 1024 + lane * 16;
+      const int row = byte / C::VROWB;
+      const int pos = (byte % C::VROWB) >> 4;
+      const int key = key0 + row;
+      const unsigned off =
+          key < L ? (unsigned)(key * C::VROWB + ((pos ^ swz_v<C::VROWB, C::V8>(row)) << 4)) : v_oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(vb + j * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  if (ntiles > 0) issue_tile(key_begin, lk0, lv0);
+
   // Q^T fragment (B operand): lane holds Q[my_q][16*kk + 8*h .. +7] for every kk.
   u32x4 qf[C::DK];
 #pragma unroll
@@ -197,76 +266,34 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
     qf[kk] = buf_load16(rq, off);
   }
 
-  // Global -> register prefetch of one K/V tile; rows at or past L come back as zeros.
-  u32x4 kreg[C::KCH], vreg[C::VCH];
-  auto load_tile = [&](int key0) {
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int chunk = tid + i * C::NT;
-      const int row = chunk / (D / 8);
-      const int cc = chunk % (D / 8);
-      const int key = key0 + row;
-      const unsigned off = (unsigned)(key < L ? (key * D + cc * 8) * 2 : head_elems * 2);
-      kreg[i] = buf_load16(rk, off);
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int chunk = tid + i * C::NT;
-      constexpr int per_row = D * C::VB / 16;
-      const int row = chunk / per_row;
-      const int cc = chunk % per_row;
-      const int key = key0 + row;
-      const unsigned off =
-          (unsigned)(key < L ? (unsigned)key * D * C::VB + cc * 16 : head_elems * C::VB);
-      vreg[i] = buf_load16(rv, off);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::KCH; ++i) {
-      const int chunk = tid + i * C::NT;
-      const int row = chunk / (D / 8);
-      const int cc = chunk % (D / 8);
-      *(u32x4*)(ldsK + row * C::KROW + cc * 16) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) {
-      const int chunk = tid + i * C::NT;
-      constexpr int per_row = D * C::VB / 16;
-      const int row = chunk / per_row;
-      const int cc = chunk % per_row;
-      *(u32x4*)(ldsV + row * C::VROW + cc * 16) = vreg[i];
-    }
-  };
-
   f32x16 acc[C::DTL];
 #pragma unroll
   for (int dt = 0; dt < C::DTL; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m_run = -INFINITY;   // running max of scores * c (log2 domain)
-  float l_run = 0.f;         // running sum of 2^(s*c - m_run) over this lane's keys
+  float m_ref = -INFINITY;   // reference max (scores * c, log2 domain) acc and l are relative to
+  float l_run = 0.f;         // running sum of 2^(s*c - m_ref) over this lane's keys
 
-  // LDS addresses that do not change across tiles.
-  const int krow_lane = key_of_row(col);
-  const unsigned char* kfrag_base = ldsK + krow_lane * C::KROW + h * 16;
+  // Per-lane LDS offsets that do not change across tiles.
+  const int krow = key_of_row(col);                       // + 32*kt for subtile kt
+  const int kswz = swz_k<C::KROWB>(krow);                 // same for krow + 32*kt
+  const int k_lane_off = krow * C::KROWB;
   // ds_read_b64_tr_b16: in each 16-lane group, lane 4e+q supplies the address of row e,
   // 4-element column block q; the instruction hands lane 4q+c element e of that block.
   const int g16 = lane >> 4, s16 = lane & 15;
-  const int tr16_row = 8 * (g16 >> 1) + (s16 >> 2);
-  const int tr16_col = 16 * (g16 & 1) + 4 * (s16 & 3);
+  const int tr16_row = 8 * (g16 >> 1) + (s16 >> 2);       // + 16*cc + 4*t
+  const int tr16_cb = 32 * (g16 & 1) + 8 * (s16 & 3);      // byte in a 64-byte d tile
   // ds_read_b64_tr_b8: lane 2e+q supplies row e, 8-byte column block q.
-  const int tr8_row = 8 * (g16 >> 1) + (s16 >> 1);
-  const int tr8_col = 16 * (g16 & 1) + 8 * (s16 & 1);
+  const int tr8_row = 8 * (g16 >> 1) + (s16 >> 1);        // + 64*u64 + 16*t4
+  const int tr8_cb = 16 * (g16 & 1) + 8 * (s16 & 1);      // byte in a 32-byte d tile
 
-  if (ntiles > 0) load_tile(key_begin);
-
-  for (int t = 0; t < ntiles; ++t) {
+  // One key tile: tile t sits in (kbuf, vbuf); tile t+1 is DMA'd into (nk, nv) meanwhile.
+  auto step = [&](int t, const unsigned char* kbuf, const unsigned char* vbuf, unsigned char* nk,
+                  unsigned char* nv) {
     const int key0 = key_begin + t * BN;
-    __syncthreads();   // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(key0 + BN);   // in flight while this tile is consumed
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA (and Q loads) landed
+    __syncthreads();                 // everyone's DMA landed; nobody still reads the other buffer
+    if (C::NBUF == 2 && t + 1 < ntiles) issue_tile(key0 + BN, nk, nv);
 
     // Which 32-key subtiles this wave needs, and which need an element mask.
     bool live[C::KT], masked[C::KT];
@@ -292,10 +319,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
       if (live[kt]) {
-        const unsigned char* kb = kfrag_base + 32 * kt * C::KROW;
+        const unsigned char* kb = kbuf + k_lane_off + 32 * kt * C::KROWB;
 #pragma unroll
         for (int kk = 0; kk < C::DK; ++kk) {
-          const u32x4 a = *(const u32x4*)(kb + kk * 32);
+          const u32x4 a = *(const u32x4*)(kb + (((2 * kk + h) ^ kswz) << 4));
           s[kt] = mfma_qk<DT>(a, qf[kk], s[kt]);
         }
       }
@@ -322,13 +349,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      for (int r = 0; r < 16; r += 2) mx = max3(mx, s[kt][r], s[kt][r + 1]);
     }
-    mx = xor32_max(mx);
+    mx = __builtin_fmaxf(mx, partner(mx));
 
     // ---- online softmax update ------------------------------------------------------------
-    const float m_new = fmaxf(m_run, mx * p.c);
-    const float neg = -m_new;
+    const float m_cand = mx * p.c;
+    if constexpr (MODE == kMaskBlock) {
+      m_ref = m_cand;                              // single tile: exact max, nothing to rescale
+    } else {
+      const bool need = m_cand > m_ref + C::TAU;   // always true on a lane's first live tile
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? m_cand : m_ref;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;  // 0 at first
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::DTL; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      }
+    }
+    const float neg = -m_ref;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt)
@@ -338,17 +380,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         s[kt][r] = e;
         psum += e;
       }
-    if constexpr (MODE == kMaskBlock) {
-      l_run = psum;   // single tile: nothing to rescale
-    } else {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first tile
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < C::DTL; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-    }
-    m_run = m_new;
+    l_run += psum;
 
     // ---- O^T += V^T * P^T -----------------------------------------------------------------
     if constexpr (!C::V8) {
@@ -361,15 +393,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         for (int w = 0; w < 4; ++w) pb[w] = pack2<DT>(s[kt][c8 + 2 * w], s[kt][c8 + 2 * w + 1]);
 #pragma unroll
         for (int dt = 0; dt < C::DTL; ++dt) {
-          const unsigned char* vb =
-              ldsV + (16 * cc + tr16_row) * C::VROW + (32 * dt + tr16_col) * 2;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vb));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vb + 4 * C::VROW));
           u32x4 a;
-          __builtin_memcpy(&a, &lo, 8);
-          __builtin_memcpy((char*)&a + 8, &hi, 8);
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int row = 16 * cc + 4 * tt + tr16_row;
+            const int byte = 64 * dt + tr16_cb;
+            const int sw = ((byte >> 4) ^ swz_v<C::VROWB, false>(row)) << 4 | (byte & 15);
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vbuf + row * C::VROWB + sw));
+            __builtin_memcpy((char*)&a + 8 * tt, &x, 8);
+          }
           acc[dt] = mfma_qk<DT>(a, pb, acc[dt]);
         }
       }
@@ -391,10 +424,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
           i32x8 a;
 #pragma unroll
           for (int t4 = 0; t4 < 4; ++t4) {
-            const unsigned char* vb =
-                ldsV + (64 * u64 + 16 * t4 + tr8_row) * C::VROW + 32 * dt + tr8_col;
+            const int row = 64 * u64 + 16 * t4 + tr8_row;
+            const int byte = 32 * dt + tr8_cb;
+            const int sw = ((byte >> 4) ^ swz_v<C::VROWB, true>(row)) << 4 | (byte & 15);
             const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (__attribute__((address_space(3))) i32x2*)(vb));
+                (__attribute__((address_space(3))) i32x2*)(vbuf + row * C::VROWB + sw));
             a[2 * t4] = x[0];
             a[2 * t4 + 1] = x[1];
           }
@@ -402,10 +436,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         }
       }
     }
+  };
+
+  // Unrolled by two so each call sees fixed buffers.
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, lk0, lv0, lk1, lv1);
+    if (t + 1 < ntiles) step(t + 1, lk1, lv1, lk0, lv0);
   }
 
   // ---- epilogue: O = acc / l, rounded to Q's type; optional natural-log normaliser -------
-  const float l_tot = xor32_sum(l_run);
+  const float l_tot = l_run + partner(l_run);
   const float inv = 1.0f / l_tot;
   if (my_q < L) {
     unsigned char* orow = p.o + ((size_t)bh * head_elems + (size_t)my_q * D) * 2;
@@ -420,7 +460,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(Params p) {
         *(u32x2*)(orow + (32 * dt + 8 * a4 + 4 * h) * 2) = w;
       }
     if (p.lse != nullptr && h == 0)
-      p.lse[(size_t)bh * L + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      p.lse[(size_t)bh * L + my_q] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
@@ -435,16 +475,7 @@ hipError_t launch(const Params& p0, hipStream_t stream) {
   p.n_qblocks = (p.L + C::BM - 1) / C::BM;
   const long long blocks = (long long)p.n_qblocks * p.bh;
   auto kern = attn_fwd_kernel<D, DT, MODE, NW, BN>;
-  if (C::LDS_BYTES > 64 * 1024) {
-    static bool raised = false;   // per instance; the attribute is process-wide
-    if (!raised) {
-      hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-      if (e != hipSuccess) return e;
-      raised = true;
-    }
-  }
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::NT), C::LDS_BYTES, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -470,7 +501,10 @@ bool supported(const Problem& pr) {
 
 attn_status_t validate(const Problem& pr) {
   if (pr.mode < 0 || pr.mode > 2 || pr.dtype < 0 || pr.dtype > 2) return ATTN_ERR_ARG;
-  if (!std::isfinite(pr.sm_scale) || !(pr.sm_scale > 0.f)) return ATTN_ERR_ARG;
+  // finite and positive, checked on the bits (independent of floating-point flags)
+  const uint32_t sbits = __builtin_bit_cast(uint32_t, pr.sm_scale);
+  const bool not_finite = ((sbits >> 23) & 0xffu) == 0xffu;
+  if (not_finite || (sbits >> 31) != 0u || (sbits & 0x7fffffffu) == 0u) return ATTN_ERR_ARG;
   if (pr.batch < 0 || pr.heads < 0 || pr.L < 0 || pr.D <= 0) return ATTN_ERR_SHAPE;
   if (pr.mode == kMaskBlock) {
     if (pr.block_size <= 0) return ATTN_ERR_SHAPE;

@@ -184,6 +184,40 @@ __device__ __forceinline__ float partner(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// One K/V tile HBM -> LDS by DMA (see the kernel for the layout).  A separate device function:
+// the same code written as a lambda inside the kernel made the host compiler drop the kernel's
+// launch stub.
+template <class C, int BN, int NW>
+__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int key0,
+                                         int L, int wave, int lane, unsigned k_oob, unsigned v_oob,
+                                         const unsigned* k_off, const unsigned* v_off,
+                                         unsigned char* kb, unsigned char* vb) {
+  const bool inside = key0 + BN <= L;   // scalar: no row of this tile is past L
+  const int k_soff = key0 * C::KROWB, v_soff = key0 * C::VROWB;
+#pragma unroll
+  for (int i = 0; i < C::KDMA; ++i) {
+    auto* dst = (__attribute__((address_space(3))) void*)(kb + (wave + i * NW) * 1024);
+    if (inside) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, k_off[i], k_soff, 0, 0);
+    } else {
+      const int row = ((wave + i * NW) * 1024 + lane * 16) / C::KROWB;
+      const unsigned off = key0 + row < L ? k_off[i] + k_soff : k_oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, off, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::VDMA; ++i) {
+    auto* dst = (__attribute__((address_space(3))) void*)(vb + (wave + i * NW) * 1024);
+    if (inside) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, v_off[i], v_soff, 0, 0);
+    } else {
+      const int row = ((wave + i * NW) * 1024 + lane * 16) / C::VROWB;
+      const unsigned off = key0 + row < L ? v_off[i] + v_soff : v_oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, off, 0, 0, 0);
+    }
+  }
+}
+
 template <int D, int DT, int MODE, int NW, int BN>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(Cfg<D, DT, MODE, NW, BN>::WAVES_PER_EU)))
@@ -228,32 +262,26 @@ void attn_fwd_kernel(Params p) {
   const int ntiles = (key_end - key_begin + BN - 1) / BN;
 
   // HBM -> LDS by DMA: instruction j of a tile fills LDS bytes [1024 j, 1024 j + 1024); lane l
-  // lands at +16 l.  The lane fetches the global chunk that the swizzle stores at that slot;
+  // lands at +16 l.  The lane fetches the global chunk that the swizzle stores at that slot.
+  // Per lane the tile-relative row and byte offset of every instruction are fixed; a tile adds
+  // key0 * row_bytes as a scalar offset.  Tiles reaching past row L take the checked path, where
   // rows at or past L read as zeros.
-  auto issue_tile = [&](int key0, unsigned char* kb, unsigned char* vb) {
+  unsigned k_off[C::KDMA], v_off[C::VDMA];
+  auto k_row = [&](int i) { return ((wave + i * NW) * 1024 + lane * 16) / C::KROWB; };
+  auto v_row = [&](int i) { return ((wave + i * NW) * 1024 + lane * 16) / C::VROWB; };
 #pragma unroll
-    for (int i = 0; i < C::KDMA; ++i) {
-      const int j = wave + i * NW;
-      const int byte = j * 1024 + lane * 16;
-      const int row = byte / C::KROWB;
-      const int pos = (byte % C::KROWB) >> 4;
-      const int key = key0 + row;
-      const unsigned off = key < L ? (unsigned)(key * C::KROWB + ((pos ^ swz_k<C::KROWB>(row)) << 4)) : k_oob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(kb + j * 1024), 16, off, 0, 0, 0);
-    }
+  for (int i = 0; i < C::KDMA; ++i) {
+    const int byte = (wave + i * NW) * 1024 + lane * 16;
+    k_off[i] = (unsigned)(k_row(i) * C::KROWB + ((((byte % C::KROWB) >> 4) ^ swz_k<C::KROWB>(k_row(i))) << 4));
+  }
 #pragma unroll
-    for (int i = 0; i < C::VDMA; ++i) {
-      const int j = wave + i * NW;
-      const int byte = j * 1024 + lane * 16;
-      const int row = byte / C::VROWB;
-      const int pos = (byte % C::VROWB) >> 4;
-      const int key = key0 + row;
-      const unsigned off =
-          key < L ? (unsigned)(key * C::VROWB + ((pos ^ swz_v<C::VROWB, C::V8>(row)) << 4)) : v_oob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)(vb + j * 1024), 16, off, 0, 0, 0);
-    }
+  for (int i = 0; i < C::VDMA; ++i) {
+    const int byte = (wave + i * NW) * 1024 + lane * 16;
+    v_off[i] = (unsigned)(v_row(i) * C::VROWB +
+                          ((((byte % C::VROWB) >> 4) ^ swz_v<C::VROWB, C::V8>(v_row(i))) << 4));
+  }
+  auto issue_tile = [&](int key0, unsigned char* kb, unsigned char* vb) __attribute__((always_inline)) {
+    dma_tile<C, BN, NW>(rk, rv, key0, L, wave, lane, k_oob, v_oob, k_off, v_off, kb, vb);
   };
 
   if (ntiles > 0) issue_tile(key_begin, lk0, lv0);
@@ -288,8 +316,11 @@ void attn_fwd_kernel(Params p) {
   const int tr8_cb = 16 * (g16 & 1) + 8 * (s16 & 1);      // byte in a 32-byte d tile
 
   // One key tile: tile t sits in (kbuf, vbuf); tile t+1 is DMA'd into (nk, nv) meanwhile.
-  auto step = [&](int t, const unsigned char* kbuf, const unsigned char* vbuf, unsigned char* nk,
-                  unsigned char* nv) {
+  // FULL: every key of the tile is visible to every query row of the workgroup (no liveness
+  // test, no mask).
+  // (FULL is a plain argument: every call passes a constant, which folds after inlining.)
+  auto step = [&](const bool FULL, int t, const unsigned char* kbuf, const unsigned char* vbuf,
+                  unsigned char* nk, unsigned char* nv) __attribute__((always_inline)) {
     const int key0 = key_begin + t * BN;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA (and Q loads) landed
     __syncthreads();                 // everyone's DMA landed; nobody still reads the other buffer
@@ -300,7 +331,10 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt) {
       const int n0 = key0 + 32 * kt;
-      if constexpr (MODE == kMaskCausal) {
+      if (FULL) {
+        live[kt] = true;
+        masked[kt] = false;
+      } else if constexpr (MODE == kMaskCausal) {
         live[kt] = n0 <= qw0 + 31;
         masked[kt] = n0 + 31 > qw0;
       } else if constexpr (MODE == kMaskNone) {
@@ -438,10 +472,22 @@ void attn_fwd_kernel(Params p) {
     }
   };
 
-  // Unrolled by two so each call sees fixed buffers.
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, lk0, lv0, lk1, lv1);
-    if (t + 1 < ntiles) step(t + 1, lk1, lv1, lk0, lv0);
+  // Tiles [0, nfull) are visible to every row of the workgroup; the rest (causal diagonal,
+  // ragged tail) take the masked path.  Even tiles live in buffer 0, odd tiles in buffer 1.
+  // The unmasked loop is unrolled by two so each copy sees fixed buffers (the compiler then
+  // knows the buffer it reads is not the one the DMA is filling); the few masked tiles pick
+  // their buffers at run time.
+  int nfull = ntiles;
+  if constexpr (MODE == kMaskCausal) nfull = min(ntiles, (m0 + 1) / BN);
+  if constexpr (MODE == kMaskNone) nfull = min(ntiles, L / BN);
+  int t = 0;
+  for (; t + 1 < nfull; t += 2) {
+    step(true, t, lk0, lv0, lk1, lv1);
+    step(true, t + 1, lk1, lv1, lk0, lv0);
+  }
+  for (; t < ntiles; ++t) {     // an odd last unmasked tile also goes this way
+    const bool odd = (C::NBUF == 2) && (t & 1);
+    step(false, t, odd ? lk1 : lk0, odd ? lv1 : lv0, odd ? lk0 : lk1, odd ? lv0 : lv1);
   }
 
   // ---- epilogue: O = acc / l, rounded to Q's type; optional natural-log normaliser -------

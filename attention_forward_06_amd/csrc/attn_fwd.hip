@@ -129,6 +129,16 @@ struct Cfg {
   static constexpr int LDS_BYTES = NBUF * (KTILE + VTILE);
   static constexpr int KDMA = KTILE / 1024 / NW;  // 1 KiB LDS-DMA instructions per wave per K tile
   static constexpr int VDMA = VTILE / 1024 / NW;
+  // Period (in DMA instruction index i) of a lane's swizzled offset: instruction i starts
+  // i * NW * 1024 / ROWB rows further on, and the swizzles only read the row modulo
+  // 16 (K), 8 (fp8 V) or 4 (16-bit V).
+  static constexpr int period(int rows_per_step, int modulus) {
+    int p = 1;
+    while ((p * rows_per_step) % modulus != 0) ++p;
+    return p;
+  }
+  static constexpr int KPER = period(NW * 1024 / KROWB, 16);
+  static constexpr int VPER = period(NW * 1024 / VROWB, V8 ? 8 : 4);
   // The accumulator is rescaled when a row max grows by more than 2^TAU over the reference
   // it was accumulated against.  TAU = 0 is the pages' recurrence (every increase rescales,
   // so the current maximum always has weight exactly 1); a wave skips the rescale only when
@@ -184,36 +194,23 @@ __device__ __forceinline__ float partner(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// One K/V tile HBM -> LDS by DMA (see the kernel for the layout).  A separate device function:
+// One tile of K or V, HBM -> LDS by DMA (see the kernel for the layout).  A device function:
 // the same code written as a lambda inside the kernel made the host compiler drop the kernel's
 // launch stub.
-template <class C, int BN, int NW>
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int key0,
-                                         int L, int wave, int lane, unsigned k_oob, unsigned v_oob,
-                                         const unsigned* k_off, const unsigned* v_off,
-                                         unsigned char* kb, unsigned char* vb) {
+template <int ROWB, int NI, int PER, int NW, int BN>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, int key0, int L, int wave, int lane,
+                                         unsigned oob, const unsigned* off, unsigned char* buf) {
   const bool inside = key0 + BN <= L;   // scalar: no row of this tile is past L
-  const int k_soff = key0 * C::KROWB, v_soff = key0 * C::VROWB;
 #pragma unroll
-  for (int i = 0; i < C::KDMA; ++i) {
-    auto* dst = (__attribute__((address_space(3))) void*)(kb + (wave + i * NW) * 1024);
+  for (int i = 0; i < NI; ++i) {
+    auto* dst = (__attribute__((address_space(3))) void*)(buf + (wave + i * NW) * 1024);
+    const int soff = key0 * ROWB + i * NW * 1024;    // scalar part of the offset
     if (inside) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, k_off[i], k_soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off[i % PER], soff, 0, 0);
     } else {
-      const int row = ((wave + i * NW) * 1024 + lane * 16) / C::KROWB;
-      const unsigned off = key0 + row < L ? k_off[i] + k_soff : k_oob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, off, 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < C::VDMA; ++i) {
-    auto* dst = (__attribute__((address_space(3))) void*)(vb + (wave + i * NW) * 1024);
-    if (inside) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, v_off[i], v_soff, 0, 0);
-    } else {
-      const int row = ((wave + i * NW) * 1024 + lane * 16) / C::VROWB;
-      const unsigned off = key0 + row < L ? v_off[i] + v_soff : v_oob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, off, 0, 0, 0);
+      const int row = ((wave + i * NW) * 1024 + lane * 16) / ROWB;
+      const unsigned o = key0 + row < L ? off[i % PER] + (unsigned)soff : oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, o, 0, 0, 0);
     }
   }
 }
@@ -266,25 +263,39 @@ void attn_fwd_kernel(Params p) {
   // Per lane the tile-relative row and byte offset of every instruction are fixed; a tile adds
   // key0 * row_bytes as a scalar offset.  Tiles reaching past row L take the checked path, where
   // rows at or past L read as zeros.
-  unsigned k_off[C::KDMA], v_off[C::VDMA];
-  auto k_row = [&](int i) { return ((wave + i * NW) * 1024 + lane * 16) / C::KROWB; };
-  auto v_row = [&](int i) { return ((wave + i * NW) * 1024 + lane * 16) / C::VROWB; };
+  // The lane's offset inside instruction i repeats with period KPER (VPER) in i, up to the
+  // 1 KiB-per-instruction stride: the swizzle only looks at low row bits.
+  unsigned k_off[C::KPER], v_off[C::VPER];
 #pragma unroll
-  for (int i = 0; i < C::KDMA; ++i) {
+  for (int i = 0; i < C::KPER; ++i) {
     const int byte = (wave + i * NW) * 1024 + lane * 16;
-    k_off[i] = (unsigned)(k_row(i) * C::KROWB + ((((byte % C::KROWB) >> 4) ^ swz_k<C::KROWB>(k_row(i))) << 4));
+    const int row = byte / C::KROWB;
+    k_off[i] = (unsigned)(row * C::KROWB + ((((byte % C::KROWB) >> 4) ^ swz_k<C::KROWB>(row)) << 4)) -
+               (unsigned)(i * NW * 1024);
   }
 #pragma unroll
-  for (int i = 0; i < C::VDMA; ++i) {
+  for (int i = 0; i < C::VPER; ++i) {
     const int byte = (wave + i * NW) * 1024 + lane * 16;
-    v_off[i] = (unsigned)(v_row(i) * C::VROWB +
-                          ((((byte % C::VROWB) >> 4) ^ swz_v<C::VROWB, C::V8>(v_row(i))) << 4));
+    const int row = byte / C::VROWB;
+    v_off[i] = (unsigned)(row * C::VROWB + ((((byte % C::VROWB) >> 4) ^ swz_v<C::VROWB, C::V8>(row)) << 4)) -
+               (unsigned)(i * NW * 1024);
   }
-  auto issue_tile = [&](int key0, unsigned char* kb, unsigned char* vb) __attribute__((always_inline)) {
-    dma_tile<C, BN, NW>(rk, rv, key0, L, wave, lane, k_oob, v_oob, k_off, v_off, kb, vb);
+  auto dma_k = [&](int key0, unsigned char* kb) __attribute__((always_inline)) {
+    dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb);
+  };
+  auto dma_v = [&](int key0, unsigned char* vb) __attribute__((always_inline)) {
+    dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb);
   };
 
-  if (ntiles > 0) issue_tile(key_begin, lk0, lv0);
+  // Software pipeline: iteration t computes the scores of tile t+1 on MFMA while the VALU runs
+  // the softmax of tile t, then P.V of tile t.  K therefore streams one tile ahead of V:
+  // tile j's K and V both live in buffer j % 2; at the top of iteration t (after the barrier)
+  // the DMA fills K(t+2) into the K buffer tile t used and V(t+1) into the V buffer of t-1.
+  if (ntiles > 0) {
+    dma_k(key_begin, lk0);
+    dma_v(key_begin, lv0);
+  }
+  if (ntiles > 1) dma_k(key_begin + BN, lk1);
 
   // Q^T fragment (B operand): lane holds Q[my_q][16*kk + 8*h .. +7] for every kk.
   u32x4 qf[C::DK];
@@ -315,19 +326,15 @@ void attn_fwd_kernel(Params p) {
   const int tr8_row = 8 * (g16 >> 1) + (s16 >> 1);        // + 64*u64 + 16*t4
   const int tr8_cb = 16 * (g16 & 1) + 8 * (s16 & 1);      // byte in a 32-byte d tile
 
-  // One key tile: tile t sits in (kbuf, vbuf); tile t+1 is DMA'd into (nk, nv) meanwhile.
-  // FULL: every key of the tile is visible to every query row of the workgroup (no liveness
-  // test, no mask).
-  // (FULL is a plain argument: every call passes a constant, which folds after inlining.)
-  auto step = [&](const bool FULL, int t, const unsigned char* kbuf, const unsigned char* vbuf,
-                  unsigned char* nk, unsigned char* nv) __attribute__((always_inline)) {
-    const int key0 = key_begin + t * BN;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA (and Q loads) landed
-    __syncthreads();                 // everyone's DMA landed; nobody still reads the other buffer
-    if (C::NBUF == 2 && t + 1 < ntiles) issue_tile(key0 + BN, nk, nv);
+  // Tiles [0, nfull) are visible to every query row of the workgroup (no liveness test, no
+  // mask); the causal diagonal and a ragged tail take the general path.
+  int nfull = ntiles;
+  if constexpr (MODE == kMaskCausal) nfull = min(ntiles, (m0 + 1) / BN);
+  if constexpr (MODE == kMaskNone) nfull = min(ntiles, L / BN);
 
-    // Which 32-key subtiles this wave needs, and which need an element mask.
-    bool live[C::KT], masked[C::KT];
+  // Which 32-key subtiles of tile j this wave needs, and which need an element mask.
+  auto tile_flags = [&](int j, const bool FULL, bool* live, bool* masked) __attribute__((always_inline)) {
+    const int key0 = key_begin + j * BN;
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt) {
       const int n0 = key0 + 32 * kt;
@@ -345,23 +352,40 @@ void attn_fwd_kernel(Params p) {
         masked[kt] = false;
       }
     }
+  };
 
-    // ---- S^T = K * Q^T ------------------------------------------------------------------
-    f32x16 s[C::KT];
+  // S^T = K * Q^T for the live subtiles of one tile, in two parts so that all K fragment reads
+  // can be issued well before the MFMAs that consume them.
+  auto k_frags = [&](u32x4 (*fr)[C::DK], const unsigned char* kbuf, const bool* live) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+    for (int kt = 0; kt < (D <= 128 ? 1 : 0); ++kt)
       if (live[kt]) {
         const unsigned char* kb = kbuf + k_lane_off + 32 * kt * C::KROWB;
 #pragma unroll
-        for (int kk = 0; kk < C::DK; ++kk) {
-          const u32x4 a = *(const u32x4*)(kb + (((2 * kk + h) ^ kswz) << 4));
-          s[kt] = mfma_qk<DT>(a, qf[kk], s[kt]);
-        }
+        for (int kk = 0; kk < C::DK; ++kk) fr[kt][kk] = *(const u32x4*)(kb + (((2 * kk + h) ^ kswz) << 4));
       }
+  };
+  auto scores = [&](f32x16* s, u32x4 (*fr)[C::DK], const unsigned char* kbuf, const bool* live) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) {
+      if (!live[kt]) continue;
+      f32x16 z;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < C::DK; ++kk) {
+        u32x4 a;
+        if (D <= 128 && kt == 0) a = fr[kt][kk];
+        else a = *(const u32x4*)(kbuf + k_lane_off + 32 * kt * C::KROWB + (((2 * kk + h) ^ kswz) << 4));
+        z = mfma_qk<DT>(a, qf[kk], z);
+      }
+      s[kt] = z;
     }
+  };
 
+  // Mask, online-softmax update and O += P.V for tile t whose scores are in s.
+  auto softmax_max = [&](int t, f32x16* s, const bool* live, const bool* masked) __attribute__((always_inline)) {
+    const int key0 = key_begin + t * BN;
     // ---- mask, row max ------------------------------------------------------------------
     // Lane's register r of subtile kt holds key key0 + 32*kt + 16*(r/8) + 8*h + r%8.
     float mx = -INFINITY;
@@ -404,6 +428,8 @@ void attn_fwd_kernel(Params p) {
           for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
       }
     }
+  };
+  auto softmax_exp = [&](f32x16* s) __attribute__((always_inline)) {
     const float neg = -m_ref;
     float psum = 0.f;
 #pragma unroll
@@ -415,7 +441,8 @@ void attn_fwd_kernel(Params p) {
         psum += e;
       }
     l_run += psum;
-
+  };
+  auto pv = [&](f32x16* s, const unsigned char* vbuf, const bool* live) __attribute__((always_inline)) {
     // ---- O^T += V^T * P^T -----------------------------------------------------------------
     if constexpr (!C::V8) {
 #pragma unroll
@@ -472,22 +499,51 @@ void attn_fwd_kernel(Params p) {
     }
   };
 
-  // Tiles [0, nfull) are visible to every row of the workgroup; the rest (causal diagonal,
-  // ragged tail) take the masked path.  Even tiles live in buffer 0, odd tiles in buffer 1.
-  // The unmasked loop is unrolled by two so each copy sees fixed buffers (the compiler then
-  // knows the buffer it reads is not the one the DMA is filling); the few masked tiles pick
-  // their buffers at run time.
-  int nfull = ntiles;
-  if constexpr (MODE == kMaskCausal) nfull = min(ntiles, (m0 + 1) / BN);
-  if constexpr (MODE == kMaskNone) nfull = min(ntiles, L / BN);
-  int t = 0;
-  for (; t + 1 < nfull; t += 2) {
-    step(true, t, lk0, lv0, lk1, lv1);
-    step(true, t + 1, lk1, lv1, lk0, lv0);
+  // One pipelined iteration; buffers are passed in so that the unrolled copies see fixed ones.
+  // fast: tiles t and t+1 are both unmasked (a constant at every call).
+  auto iteration = [&](const bool fast, int t, f32x16* s_cur, f32x16* s_nxt,
+                       const unsigned char* kb_nxt, const unsigned char* vb_cur, unsigned char* kb_dma,
+                       unsigned char* vb_dma) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA of K(t+1), V(t) landed
+    __syncthreads();                 // everyone's did; nobody still reads K(t) or V(t-1)
+    if (t + 2 < ntiles) dma_k(key_begin + (t + 2) * BN, kb_dma);
+    if (t + 1 < ntiles) dma_v(key_begin + (t + 1) * BN, vb_dma);
+    const bool has_next = t + 1 < ntiles;
+    bool live_n[C::KT], masked_n[C::KT];
+    u32x4 fr[C::KT][C::DK];
+    if (has_next) {
+      tile_flags(t + 1, fast || t + 1 < nfull, live_n, masked_n);
+      k_frags(fr, kb_nxt, live_n);             // K(t+1) reads, in flight during the max below
+    }
+    bool live[C::KT], masked[C::KT];
+    tile_flags(t, fast || t < nfull, live, masked);
+    softmax_max(t, s_cur, live, masked);       // VALU: mask, row max, rescale
+    if (has_next) scores(s_nxt, fr, kb_nxt, live_n);   // MFMA: S(t+1) ...
+    softmax_exp(s_cur);                        // ... while the VALU exponentiates P(t)
+    pv(s_cur, vb_cur, live);                   // MFMA: O += P(t) V(t)
+  };
+
+  f32x16 sA[C::KT], sB[C::KT];
+  if (ntiles > 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    bool live0[C::KT], masked0[C::KT];
+    tile_flags(0, 0 < nfull, live0, masked0);
+    u32x4 fr0[C::KT][C::DK];
+    k_frags(fr0, lk0, live0);
+    scores(sA, fr0, lk0, live0);
   }
-  for (; t < ntiles; ++t) {     // an odd last unmasked tile also goes this way
+  int t = 0;
+  // Unmasked iterations (tiles t and t+1 both unmasked) in pairs with fixed buffers.
+  for (; t + 2 < nfull; t += 2) {
+    iteration(true, t, sA, sB, lk1, lv0, lk0, lv1);
+    iteration(true, t + 1, sB, sA, lk0, lv1, lk1, lv0);
+  }
+  for (; t < ntiles; ++t) {
     const bool odd = (C::NBUF == 2) && (t & 1);
-    step(false, t, odd ? lk1 : lk0, odd ? lv1 : lv0, odd ? lk0 : lk1, odd ? lv0 : lv1);
+    iteration(false, t, sA, sB, odd ? lk0 : lk1, odd ? lv1 : lv0, odd ? lk1 : lk0, odd ? lv0 : lv1);
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) sA[kt] = sB[kt];
   }
 
   // ---- epilogue: O = acc / l, rounded to Q's type; optional natural-log normaliser -------

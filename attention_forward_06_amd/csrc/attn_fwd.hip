@@ -104,6 +104,18 @@ __device__ __forceinline__ unsigned pack2(float lo, float hi) {
   else return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
+// acc + (lo + hi) of a packed 16-bit pair (v_dot2 against (1, 1)).
+template <int DT>
+__device__ __forceinline__ float sum2_acc(unsigned packed, float acc) {
+  if constexpr (DT == kF16) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), one, acc, false);
+  } else {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), one, acc, false);
+  }
+}
+
 // MFMA row rho of the S^T = K * Q^T product reads key pi(rho): bits 2 and 3 swapped.
 __device__ __forceinline__ int key_of_row(int rho) {
   return (rho & 0x13) | ((rho & 4) << 1) | ((rho >> 1) & 4);
@@ -139,12 +151,16 @@ struct Cfg {
   }
   static constexpr int KPER = period(NW * 1024 / KROWB, 16);
   static constexpr int VPER = period(NW * 1024 / VROWB, V8 ? 8 : 4);
-  // The accumulator is rescaled when a row max grows by more than 2^TAU over the reference
-  // it was accumulated against.  TAU = 0 is the pages' recurrence (every increase rescales,
-  // so the current maximum always has weight exactly 1); a wave skips the rescale only when
-  // no row of it saw a larger maximum.  (A positive TAU trades exactness of the dominant
-  // weight, which bf16 P then rounds, for fewer rescales.)
-  static constexpr float TAU = 0.f;
+  // The accumulator is rescaled when a row max grows by more than 2^TAU over the reference it
+  // was accumulated against (exact in real arithmetic: O = acc / l in a common frame); a wave
+  // skips the rescale when no row of it needs one.  The fp8 path uses TAU = 0, the pages'
+  // recurrence, so P is rounded against the running maximum exactly as the pages do.
+  static constexpr float TAU = V8 ? 0.f : 8.f;
+  // 16-bit P: O is normalised by the sum of the rounded weights P^ that P.V actually used.
+  // O = sum P^ v / sum P^ is then an exactly normalised average of the V rows -- exact for a
+  // single dominant key and for constant V -- which is what makes the capped rescale above safe.
+  // The fp8 path keeps the pages' sum over the unrounded p (P is far coarser there).
+  static constexpr bool HAT = !V8;
   static constexpr int WAVES_PER_EU = (D >= 256) ? 1 : 2;
   static_assert(BN % 32 == 0, "key tile is a whole number of 32-key subtiles");
   static_assert(!V8 || BN % 64 == 0, "fp8 P.V consumes 64 keys per MFMA");
@@ -215,7 +231,7 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, int key0, int
   }
 }
 
-template <int D, int DT, int MODE, int NW, int BN>
+template <int D, int DT, int MODE, int NW, int BN, bool LSE>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(Cfg<D, DT, MODE, NW, BN>::WAVES_PER_EU)))
 void attn_fwd_kernel(Params p) {
@@ -311,7 +327,8 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float m_ref = -INFINITY;   // reference max (scores * c, log2 domain) acc and l are relative to
-  float l_run = 0.f;         // running sum of 2^(s*c - m_ref) over this lane's keys
+  float l_run = 0.f;         // running sum of 2^(s*c - m_ref) over this lane's keys (unrounded)
+  float l_hat = 0.f;         // the same over the rounded 16-bit weights (16-bit P only)
 
   // Per-lane LDS offsets that do not change across tiles.
   const int krow = key_of_row(col);                       // + 32*kt for subtile kt
@@ -422,6 +439,7 @@ void attn_fwd_kernel(Params p) {
         const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;  // 0 at first
         m_ref = m_new;
         l_run *= alpha;
+        l_hat *= alpha;
 #pragma unroll
         for (int dt = 0; dt < C::DTL; ++dt)
 #pragma unroll
@@ -429,29 +447,48 @@ void attn_fwd_kernel(Params p) {
       }
     }
   };
-  auto softmax_exp = [&](f32x16* s) __attribute__((always_inline)) {
+  // P = 2^(s c - m_ref).  16-bit: packed right away into pk (the P.V operand) with the sum of
+  // the rounded pairs; the unrounded sum only when the log-normaliser is requested.
+  auto softmax_exp = [&](f32x16* s, u32x4* pk, const bool* live) __attribute__((always_inline)) {
     const float neg = -m_ref;
-    float psum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], p.c, neg));
-        s[kt][r] = e;
-        psum += e;
-      }
-    l_run += psum;
-  };
-  auto pv = [&](f32x16* s, const unsigned char* vbuf, const bool* live) __attribute__((always_inline)) {
-    // ---- O^T += V^T * P^T -----------------------------------------------------------------
-    if constexpr (!C::V8) {
+    if constexpr (C::HAT) {
+      float lh = 0.f, le = 0.f;
 #pragma unroll
       for (int cc = 0; cc < BN / 16; ++cc) {
         const int kt = cc >> 1, c8 = (cc & 1) * 8;
         if (!live[kt]) continue;
-        u32x4 pb;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) pb[w] = pack2<DT>(s[kt][c8 + 2 * w], s[kt][c8 + 2 * w + 1]);
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][c8 + 2 * w], p.c, neg));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][c8 + 2 * w + 1], p.c, neg));
+          pk[cc][w] = pack2<DT>(e0, e1);
+          lh = sum2_acc<DT>(pk[cc][w], lh);
+          if constexpr (LSE) le += e0 + e1;
+        }
+      }
+      l_hat += lh;
+      if constexpr (LSE) l_run += le;
+    } else {
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], p.c, neg));
+          s[kt][r] = e;
+          psum += e;
+        }
+      l_run += psum;
+    }
+  };
+  auto pv = [&](f32x16* s, const u32x4* pk, const unsigned char* vbuf, const bool* live) __attribute__((always_inline)) {
+    // ---- O^T += V^T * P^T -----------------------------------------------------------------
+    if constexpr (!C::V8) {
+#pragma unroll
+      for (int cc = 0; cc < BN / 16; ++cc) {
+        const int kt = cc >> 1;
+        if (!live[kt]) continue;
+        const u32x4 pb = pk[cc];
 #pragma unroll
         for (int dt = 0; dt < C::DTL; ++dt) {
           u32x4 a;
@@ -519,8 +556,9 @@ void attn_fwd_kernel(Params p) {
     tile_flags(t, fast || t < nfull, live, masked);
     softmax_max(t, s_cur, live, masked);       // VALU: mask, row max, rescale
     if (has_next) scores(s_nxt, fr, kb_nxt, live_n);   // MFMA: S(t+1) ...
-    softmax_exp(s_cur);                        // ... while the VALU exponentiates P(t)
-    pv(s_cur, vb_cur, live);                   // MFMA: O += P(t) V(t)
+    u32x4 pk[BN / 16];
+    softmax_exp(s_cur, pk, live);              // ... while the VALU exponentiates P(t)
+    pv(s_cur, pk, vb_cur, live);               // MFMA: O += P(t) V(t)
   };
 
   f32x16 sA[C::KT], sB[C::KT];
@@ -547,8 +585,9 @@ void attn_fwd_kernel(Params p) {
   }
 
   // ---- epilogue: O = acc / l, rounded to Q's type; optional natural-log normaliser -------
-  const float l_tot = l_run + partner(l_run);
-  const float inv = 1.0f / l_tot;
+  const float l_norm = C::HAT ? l_hat : l_run;
+  const float inv = 1.0f / (l_norm + partner(l_norm));
+  const float l_exact = LSE ? l_run + partner(l_run) : 0.f;   // (all lanes take part)
   if (my_q < L) {
     unsigned char* orow = p.o + ((size_t)bh * head_elems + (size_t)my_q * D) * 2;
 #pragma unroll
@@ -561,8 +600,7 @@ void attn_fwd_kernel(Params p) {
         w[1] = pack2<DT == kF16 ? kF16 : kBF16>(acc[dt][4 * a4 + 2] * inv, acc[dt][4 * a4 + 3] * inv);
         *(u32x2*)(orow + (32 * dt + 8 * a4 + 4 * h) * 2) = w;
       }
-    if (p.lse != nullptr && h == 0)
-      p.lse[(size_t)bh * L + my_q] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (LSE && h == 0) p.lse[(size_t)bh * L + my_q] = (m_ref + __builtin_amdgcn_logf(l_exact)) * kLn2;
   }
 }
 
@@ -576,8 +614,12 @@ hipError_t launch(const Params& p0, hipStream_t stream) {
   Params p = p0;
   p.n_qblocks = (p.L + C::BM - 1) / C::BM;
   const long long blocks = (long long)p.n_qblocks * p.bh;
-  auto kern = attn_fwd_kernel<D, DT, MODE, NW, BN>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(C::NT), 0, stream, p);
+  if (p.lse != nullptr)
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MODE, NW, BN, true>), dim3((unsigned)blocks), dim3(C::NT),
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MODE, NW, BN, false>), dim3((unsigned)blocks),
+                       dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -628,11 +670,11 @@ attn_status_t validate(const Problem& pr) {
 
 template <int D, int DT>
 hipError_t dispatch_dense(int mode, const Params& p, hipStream_t s) {
-  // D = 64: 8 waves (256 query rows) and 128-key tiles per step measured fastest; D = 128
-  // and 256: 4 waves and 64-key tiles (register budget of two waves per SIMD).
+  // D = 64: 8 waves (256 query rows per workgroup, half the K/V streaming per query); D = 128
+  // and 256: 4 waves.  64-key tiles throughout (register budget of two waves per SIMD).
   if constexpr (D == 64) {
-    if (mode == kMaskCausal) return launch<D, DT, kMaskCausal, 8, 128>(p, s);
-    return launch<D, DT, kMaskNone, 8, 128>(p, s);
+    if (mode == kMaskCausal) return launch<D, DT, kMaskCausal, 8, 64>(p, s);
+    return launch<D, DT, kMaskNone, 8, 64>(p, s);
   } else {
     if (mode == kMaskCausal) return launch<D, DT, kMaskCausal, 4, 64>(p, s);
     return launch<D, DT, kMaskNone, 4, 64>(p, s);

@@ -124,11 +124,13 @@ __device__ __forceinline__ int key_of_row(int rho) {
 __device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32); }
 
-template <int D, int DT, int MODE, int NW, int BN>
+template <int D, int DT, int MODE, int NW, int BN, int KW = BN>
 struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int BM = 32 * NW;
-  static constexpr int KT = BN / 32;          // 32-key subtiles per tile
+  // KW: keys one wave works on per tile.  KW = BN except for block_diag with blocks smaller
+  // than the tile, where each wave only touches its own diagonal block inside the tile.
+  static constexpr int KT = KW / 32;          // 32-key subtiles a wave computes per tile
   static constexpr int DK = D / 16;           // 16-wide d chunks of Q.K
   static constexpr int DTL = D / 32;          // 32-wide d tiles of O
   static constexpr bool V8 = (DT == kBF16V8);
@@ -231,11 +233,11 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, int key0, int
   }
 }
 
-template <int D, int DT, int MODE, int NW, int BN, bool LSE>
+template <int D, int DT, int MODE, int NW, int BN, int KW, bool LSE>
 __global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(Cfg<D, DT, MODE, NW, BN>::WAVES_PER_EU)))
+__attribute__((amdgpu_waves_per_eu(Cfg<D, DT, MODE, NW, BN, KW>::WAVES_PER_EU)))
 void attn_fwd_kernel(Params p) {
-  using C = Cfg<D, DT, MODE, NW, BN>;
+  using C = Cfg<D, DT, MODE, NW, BN, KW>;
   // One statically sized LDS array per tile buffer, so the compiler can tell the buffer being
   // read from the one the DMA is filling (it then does not wait for that DMA before reading).
   __shared__ __attribute__((aligned(1024))) unsigned char lk0[C::KTILE];
@@ -330,17 +332,20 @@ void attn_fwd_kernel(Params p) {
   float l_run = 0.f;         // running sum of 2^(s*c - m_ref) over this lane's keys (unrounded)
   float l_hat = 0.f;         // the same over the rounded 16-bit weights (16-bit P only)
 
+  // block_diag with blocks smaller than the tile: this wave's block is rows [wrow, wrow + KW)
+  // of the tile (the workgroup's 128 rows hold 128 / KW diagonal blocks, wave-aligned).
+  const int wrow = (MODE == kMaskBlock && KW < BN) ? (32 * wave / KW) * KW : 0;
   // Per-lane LDS offsets that do not change across tiles.
-  const int krow = key_of_row(col);                       // + 32*kt for subtile kt
+  const int krow = key_of_row(col) + wrow;                // + 32*kt for subtile kt
   const int kswz = swz_k<C::KROWB>(krow);                 // same for krow + 32*kt
   const int k_lane_off = krow * C::KROWB;
   // ds_read_b64_tr_b16: in each 16-lane group, lane 4e+q supplies the address of row e,
   // 4-element column block q; the instruction hands lane 4q+c element e of that block.
   const int g16 = lane >> 4, s16 = lane & 15;
-  const int tr16_row = 8 * (g16 >> 1) + (s16 >> 2);       // + 16*cc + 4*t
+  const int tr16_row = 8 * (g16 >> 1) + (s16 >> 2) + wrow;  // + 16*cc + 4*t
   const int tr16_cb = 32 * (g16 & 1) + 8 * (s16 & 3);      // byte in a 64-byte d tile
   // ds_read_b64_tr_b8: lane 2e+q supplies row e, 8-byte column block q.
-  const int tr8_row = 8 * (g16 >> 1) + (s16 >> 1);        // + 64*u64 + 16*t4
+  const int tr8_row = 8 * (g16 >> 1) + (s16 >> 1) + wrow;  // + 64*u64 + 16*t4
   const int tr8_cb = 16 * (g16 & 1) + 8 * (s16 & 1);      // byte in a 32-byte d tile
 
   // Tiles [0, nfull) are visible to every query row of the workgroup (no liveness test, no
@@ -348,6 +353,7 @@ void attn_fwd_kernel(Params p) {
   int nfull = ntiles;
   if constexpr (MODE == kMaskCausal) nfull = min(ntiles, (m0 + 1) / BN);
   if constexpr (MODE == kMaskNone) nfull = min(ntiles, L / BN);
+
 
   // Which 32-key subtiles of tile j this wave needs, and which need an element mask.
   auto tile_flags = [&](int j, const bool FULL, bool* live, bool* masked) __attribute__((always_inline)) {
@@ -454,7 +460,7 @@ void attn_fwd_kernel(Params p) {
     if constexpr (C::HAT) {
       float lh = 0.f, le = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < BN / 16; ++cc) {
+      for (int cc = 0; cc < KW / 16; ++cc) {
         const int kt = cc >> 1, c8 = (cc & 1) * 8;
         if (!live[kt]) continue;
 #pragma unroll
@@ -485,7 +491,7 @@ void attn_fwd_kernel(Params p) {
     // ---- O^T += V^T * P^T -----------------------------------------------------------------
     if constexpr (!C::V8) {
 #pragma unroll
-      for (int cc = 0; cc < BN / 16; ++cc) {
+      for (int cc = 0; cc < KW / 16; ++cc) {
         const int kt = cc >> 1;
         if (!live[kt]) continue;
         const u32x4 pb = pk[cc];
@@ -506,7 +512,7 @@ void attn_fwd_kernel(Params p) {
       }
     } else {
 #pragma unroll
-      for (int u64 = 0; u64 < BN / 64; ++u64) {
+      for (int u64 = 0; u64 < KW / 64; ++u64) {
         if (!live[2 * u64] && !live[2 * u64 + 1]) continue;
         // P bytes: byte 16*u + r <- subtile 2*u64+u, register r (key 16*(2u + r/8) + 8h + r%8).
         i32x8 pb;
@@ -556,7 +562,7 @@ void attn_fwd_kernel(Params p) {
     tile_flags(t, fast || t < nfull, live, masked);
     softmax_max(t, s_cur, live, masked);       // VALU: mask, row max, rescale
     if (has_next) scores(s_nxt, fr, kb_nxt, live_n);   // MFMA: S(t+1) ...
-    u32x4 pk[BN / 16];
+    u32x4 pk[KW / 16];
     softmax_exp(s_cur, pk, live);              // ... while the VALU exponentiates P(t)
     pv(s_cur, pk, vb_cur, live);               // MFMA: O += P(t) V(t)
   };
@@ -608,17 +614,17 @@ void attn_fwd_kernel(Params p) {
 // Host side: validation, instance table, launch.
 // ------------------------------------------------------------------------------------------
 
-template <int D, int DT, int MODE, int NW, int BN>
+template <int D, int DT, int MODE, int NW, int BN, int KW = BN>
 hipError_t launch(const Params& p0, hipStream_t stream) {
-  using C = Cfg<D, DT, MODE, NW, BN>;
+  using C = Cfg<D, DT, MODE, NW, BN, KW>;
   Params p = p0;
   p.n_qblocks = (p.L + C::BM - 1) / C::BM;
   const long long blocks = (long long)p.n_qblocks * p.bh;
   if (p.lse != nullptr)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MODE, NW, BN, true>), dim3((unsigned)blocks), dim3(C::NT),
-                       0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MODE, NW, BN, KW, true>), dim3((unsigned)blocks),
+                       dim3(C::NT), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MODE, NW, BN, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MODE, NW, BN, KW, false>), dim3((unsigned)blocks),
                        dim3(C::NT), 0, stream, p);
   return hipGetLastError();
 }
@@ -683,9 +689,12 @@ hipError_t dispatch_dense(int mode, const Params& p, hipStream_t s) {
 
 template <int D, int DT>
 hipError_t dispatch_block(int64_t bs, const Params& p, hipStream_t s) {
-  if (bs == 32) return launch<D, DT, kMaskBlock, 1, 32>(p, s);
-  if (bs == 64) return launch<D, DT, kMaskBlock, 2, 64>(p, s);
-  return launch<D, DT, kMaskBlock, 4, 128>(p, s);
+  // Every block size runs 128 query rows (4 waves) per workgroup: 128 / bs diagonal blocks
+  // behind one 128-row K/V transfer (larger transfers keep more bytes in flight); each wave
+  // works on the bs keys of its own block.
+  if (bs == 32) return launch<D, DT, kMaskBlock, 4, 128, 32>(p, s);
+  if (bs == 64) return launch<D, DT, kMaskBlock, 4, 128, 64>(p, s);
+  return launch<D, DT, kMaskBlock, 4, 128, 128>(p, s);
 }
 
 hipError_t dispatch(const Problem& pr, const Params& p, hipStream_t s) {

@@ -66,6 +66,7 @@ struct Params {
   int L;
   int bh;          // batch * heads
   int n_qblocks;   // query blocks per (batch, head)
+  int group;       // causal: heads per longest-first group within an XCD (see block_coords)
   float c;         // sm_scale * log2(e)
 };
 
@@ -189,12 +190,23 @@ __device__ __forceinline__ int swz_v(int r) {
 }
 
 // Workgroup id -> (batch*head, query block).  Ids are dealt round-robin to the 8 XCDs;
-// the remap gives each XCD a contiguous range of (batch*head, query block) pairs so one
-// head's K/V is shared in one L2.  Causal blocks run last-query-block first (most work).
-__device__ __forceinline__ void block_coords(int id, int total, int nqb, bool heavy_first, int& bh,
-                                             int& qb) {
+// the remap gives each XCD a contiguous range of heads, so one head's K/V is shared in one L2.
+// Causal query blocks differ in length (block qb walks qb + 1 key blocks), so an XCD runs its
+// heads in groups of `group`, all query blocks of a group longest first: the blocks that start
+// last are short and the XCD's CUs finish together.  The host sizes the group so that its K/V
+// stays near the XCD's L2 capacity.
+__device__ __forceinline__ void block_coords(int id, int total, int nqb, bool heavy_first, int group,
+                                             int& bh, int& qb) {
+  const int per_xcd = total >> 3;
+  if ((total & 7) == 0 && heavy_first && per_xcd % (nqb * group) == 0) {
+    const int x = id & 7, j = id >> 3;
+    const int g = j / (group * nqb), r = j - g * (group * nqb);
+    qb = nqb - 1 - r / group;
+    bh = x * (per_xcd / nqb) + g * group + r % group;
+    return;
+  }
   int logical = id;
-  if ((total & 7) == 0) logical = (id & 7) * (total >> 3) + (id >> 3);
+  if ((total & 7) == 0) logical = (id & 7) * per_xcd + (id >> 3);
   bh = logical / nqb;
   qb = logical - bh * nqb;
   if (heavy_first) qb = nqb - 1 - qb;
@@ -252,7 +264,7 @@ void attn_fwd_kernel(Params p) {
   const int col = lane & 31;      // the lane's query within the wave's 32
 
   int bh, qb;
-  block_coords(blockIdx.x, gridDim.x, p.n_qblocks, MODE == kMaskCausal, bh, qb);
+  block_coords(blockIdx.x, gridDim.x, p.n_qblocks, MODE == kMaskCausal, p.group, bh, qb);
   const int L = p.L;
   const int m0 = qb * C::BM;              // first query row of the workgroup
   const int qw0 = m0 + 32 * wave;         // first query row of this wave
@@ -583,11 +595,11 @@ void attn_fwd_kernel(Params p) {
     iteration(true, t, sA, sB, lk1, lv0, lk0, lv1);
     iteration(true, t + 1, sB, sA, lk0, lv1, lk1, lv0);
   }
-  for (; t < ntiles; ++t) {
-    const bool odd = (C::NBUF == 2) && (t & 1);
-    iteration(false, t, sA, sB, odd ? lk0 : lk1, odd ? lv1 : lv0, odd ? lk1 : lk0, odd ? lv0 : lv1);
-#pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt) sA[kt] = sB[kt];
+  // The rest (t is even here), also in pairs with fixed buffers: with buffers chosen at run time
+  // the compiler cannot tell the DMA target from the buffer read and waits for the DMA first.
+  for (; t < ntiles; t += 2) {
+    iteration(false, t, sA, sB, lk1, lv0, lk0, lv1);
+    if (t + 1 < ntiles) iteration(false, t + 1, sB, sA, lk0, lv1, lk1, lv0);
   }
 
   // ---- epilogue: O = acc / l, rounded to Q's type; optional natural-log normaliser -------
@@ -620,6 +632,17 @@ hipError_t launch(const Params& p0, hipStream_t stream) {
   Params p = p0;
   p.n_qblocks = (p.L + C::BM - 1) / C::BM;
   const long long blocks = (long long)p.n_qblocks * p.bh;
+  // causal head groups: the largest divisor of the heads per XCD whose K/V fits in 8 MiB
+  p.group = 1;
+  if (MODE == kMaskCausal && p.bh % 8 == 0) {
+    const long long head_kv = (long long)p.L * D * (2 + C::VB);
+    const int hx = p.bh / 8;
+    for (int g = hx; g >= 1; --g)
+      if (hx % g == 0 && g * head_kv <= (8ll << 20)) {
+        p.group = g;
+        break;
+      }
+  }
   if (p.lse != nullptr)
     hipLaunchKernelGGL((attn_fwd_kernel<D, DT, MODE, NW, BN, KW, true>), dim3((unsigned)blocks),
                        dim3(C::NT), 0, stream, p);

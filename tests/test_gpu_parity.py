@@ -224,6 +224,30 @@ def test_lse_output(mode, D, dtype, bs, L):
     assert err <= 1e-4
 
 
+@pytest.mark.parametrize("B,H,L,D,dtype,mode", [
+    (4, 32, 4096, 128, "bf16", "causal"),   # 16 heads per XCD, longest-first head groups
+    (2, 8, 1024, 64, "f16", "causal"),
+    (1, 8, 600, 128, "bf16", "causal"),
+    (3, 5, 300, 64, "f16", "causal"),       # batch*heads not a multiple of 8
+    (2, 8, 1000, 128, "f16", "none"),
+])
+def test_every_query_block_of_every_head_written(B, H, L, D, dtype, mode):
+    # V is constant over keys within a head, with a value naming the head: every output row of
+    # head (b, h) is then exactly that value (weights summing to one times a constant), whatever
+    # the mask.  The output starts as NaN, so a block that is never written, or written with
+    # another head's result, fails.
+    q, k, _ = gpu_qkv(B, H, L, D, dtype, seed=5)
+    tdt = q.dtype
+    val = (1.0 + torch.arange(B * H, dtype=torch.float32).reshape(B, H, 1, 1)) / 64.0
+    v = val.expand(B, H, L, D).to(tdt).contiguous().cuda()
+    out = torch.full((B, H, L, D), float("nan"), dtype=tdt, device="cuda")
+    binding.attn_fwd(q, k, v, mask=mode, out=out)
+    torch.cuda.synchronize()
+    want = val.expand(B, H, L, D).to(tdt).cuda()
+    bad = (out != want)
+    assert not bad.any(), f"{int(bad.sum())} outputs differ; first at {bad.nonzero()[0].tolist()}"
+
+
 def test_side_stream_and_untouched_neighbours():
     D, L = 128, 256
     q, k, v = gpu_qkv(1, 2, L, D, "bf16", seed=9)

@@ -227,10 +227,11 @@ __device__ __forceinline__ float partner(float x) {
 // One tile of K or V, HBM -> LDS by DMA (see the kernel for the layout).  A device function:
 // the same code written as a lambda inside the kernel made the host compiler drop the kernel's
 // launch stub.
+// inside: the caller knows the whole tile lies below row L (no per-row check).
 template <int ROWB, int NI, int PER, int NW, int BN>
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, int key0, int L, int wave, int lane,
-                                         unsigned oob, const unsigned* off, unsigned char* buf) {
-  const bool inside = key0 + BN <= L;   // scalar: no row of this tile is past L
+                                         unsigned oob, const unsigned* off, unsigned char* buf,
+                                         const bool inside) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     auto* dst = (__attribute__((address_space(3))) void*)(buf + (wave + i * NW) * 1024);
@@ -310,11 +311,14 @@ void attn_fwd_kernel(Params p) {
     v_off[i] = (unsigned)(row * C::VROWB + ((((byte % C::VROWB) >> 4) ^ swz_v<C::VROWB, C::V8>(row)) << 4)) -
                (unsigned)(i * NW * 1024);
   }
+  // One scalar branch per tile selects the unchecked copy when no row of the tile is past L.
   auto dma_k = [&](int key0, unsigned char* kb) __attribute__((always_inline)) {
-    dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb);
+    if (key0 + BN <= L) dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb, true);
+    else dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb, false);
   };
   auto dma_v = [&](int key0, unsigned char* vb) __attribute__((always_inline)) {
-    dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb);
+    if (key0 + BN <= L) dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, true);
+    else dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, false);
   };
 
   // Software pipeline: iteration t computes the scores of tile t+1 on MFMA while the VALU runs
@@ -577,6 +581,35 @@ void attn_fwd_kernel(Params p) {
     u32x4 pk[KW / 16];
     softmax_exp(s_cur, pk, live);              // ... while the VALU exponentiates P(t)
     pv(s_cur, pk, vb_cur, live);               // MFMA: O += P(t) V(t)
+    if constexpr (D <= 128 && C::KT == 2 && !C::V8 && MODE != kMaskBlock) {
+      if (fast && has_next) {
+        // Issue order of the unmasked iteration: each score MFMA of subtile 0 followed by one K
+        // read of subtile 1, each of subtile 1 by two V^T reads, each P.V MFMA by one more V^T
+        // read, with the exponentials spread over the score MFMAs.  Every LDS read is then
+        // issued several MFMAs ahead of its use.
+        constexpr int NP = (KW / 16) * C::DTL, NV_LATE = 2 * NP - 2 * C::DK;
+        static_assert(NV_LATE == NP, "one late V^T read per P.V MFMA");
+        constexpr int VS = 32 / C::DK, VP = 32 / NP;
+#pragma unroll
+        for (int i = 0; i < C::DK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VS, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::DK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VS, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VP, 0);
+        }
+      }
+    }
   };
 
   f32x16 sA[C::KT], sB[C::KT];

@@ -31,7 +31,8 @@
 //   * K/V tiles are staged HBM -> VGPR -> LDS with 128-bit buffer loads (rows past L read as
 //     zero), prefetching tile t+1 while tile t is consumed.
 //   * Workgroup ids are remapped so all query blocks of one (batch, head) land on the same
-//     XCD (its K/V stays in that XCD's L2), heaviest causal blocks first.
+//     XCD (its K/V stays in that XCD's L2); causal blocks run longest first within small head
+//     groups, so the CUs of an XCD finish together.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -189,12 +190,11 @@ __device__ __forceinline__ int swz_v(int r) {
   else return 4 * (r & 3);
 }
 
-// Workgroup id -> (batch*head, query block).  Ids are dealt round-robin to the 8 XCDs;
-// the remap gives each XCD a contiguous range of heads, so one head's K/V is shared in one L2.
-// Causal query blocks differ in length (block qb walks qb + 1 key blocks), so an XCD runs its
-// heads in groups of `group`, all query blocks of a group longest first: the blocks that start
-// last are short and the XCD's CUs finish together.  The host sizes the group so that its K/V
-// stays near the XCD's L2 capacity.
+// Workgroup id -> (batch*head, query block).  Ids are dealt round-robin to the 8 XCDs; the remap
+// gives each XCD a contiguous range of heads, so one head's K/V is shared in one L2.  Causal query
+// blocks differ in length (block qb walks qb + 1 key blocks), so an XCD runs its heads in groups
+// of `group`, all query blocks of a group longest first: the blocks that start last are short
+// and the XCD's CUs finish together.  The host sizes the group so that its K/V fits the L2.
 __device__ __forceinline__ void block_coords(int id, int total, int nqb, bool heavy_first, int group,
                                              int& bh, int& qb) {
   const int per_xcd = total >> 3;
@@ -280,15 +280,6 @@ void attn_fwd_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, (unsigned)(head_elems * C::VB));
   const unsigned k_oob = (unsigned)(head_elems * 2), v_oob = (unsigned)(head_elems * C::VB);
 
-  // Key range walked by this workgroup.
-  int key_begin = 0, key_end = L;
-  if constexpr (MODE == kMaskCausal) key_end = min(L, m0 + C::BM);
-  if constexpr (MODE == kMaskBlock) {
-    key_begin = m0;
-    key_end = m0 + C::BM;
-  }
-  const int ntiles = (key_end - key_begin + BN - 1) / BN;
-
   // HBM -> LDS by DMA: instruction j of a tile fills LDS bytes [1024 j, 1024 j + 1024); lane l
   // lands at +16 l.  The lane fetches the global chunk that the swizzle stores at that slot.
   // Per lane the tile-relative row and byte offset of every instruction are fixed; a tile adds
@@ -320,6 +311,15 @@ void attn_fwd_kernel(Params p) {
     if (key0 + BN <= L) dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, true);
     else dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, false);
   };
+
+  // Key range walked by this workgroup.
+  int key_begin = 0, key_end = L;
+  if constexpr (MODE == kMaskCausal) key_end = min(L, m0 + C::BM);
+  if constexpr (MODE == kMaskBlock) {
+    key_begin = m0;
+    key_end = m0 + C::BM;
+  }
+  const int ntiles = (key_end - key_begin + BN - 1) / BN;
 
   // Software pipeline: iteration t computes the scores of tile t+1 on MFMA while the VALU runs
   // the softmax of tile t, then P.V of tile t.  K therefore streams one tile ahead of V:
@@ -395,16 +395,18 @@ void attn_fwd_kernel(Params p) {
 
   // S^T = K * Q^T for the live subtiles of one tile, in two parts so that all K fragment reads
   // can be issued well before the MFMAs that consume them.
-  auto k_frags = [&](u32x4 (*fr)[C::DK], const unsigned char* kbuf, const bool* live) __attribute__((always_inline)) {
+  // ksw: the lane's K swizzle (kswz); the masked iterations pass an opaque copy so that their
+  // read addresses are recomputed instead of being held in registers across the loops.
+  auto k_frags = [&](u32x4 (*fr)[C::DK], const unsigned char* kbuf, const bool* live, int ksw) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < (D <= 128 ? 1 : 0); ++kt)
       if (live[kt]) {
         const unsigned char* kb = kbuf + k_lane_off + 32 * kt * C::KROWB;
 #pragma unroll
-        for (int kk = 0; kk < C::DK; ++kk) fr[kt][kk] = *(const u32x4*)(kb + (((2 * kk + h) ^ kswz) << 4));
+        for (int kk = 0; kk < C::DK; ++kk) fr[kt][kk] = *(const u32x4*)(kb + (((2 * kk + h) ^ ksw) << 4));
       }
   };
-  auto scores = [&](f32x16* s, u32x4 (*fr)[C::DK], const unsigned char* kbuf, const bool* live) __attribute__((always_inline)) {
+  auto scores = [&](f32x16* s, u32x4 (*fr)[C::DK], const unsigned char* kbuf, const bool* live, int ksw) __attribute__((always_inline)) {
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt) {
       if (!live[kt]) continue;
@@ -415,7 +417,7 @@ void attn_fwd_kernel(Params p) {
       for (int kk = 0; kk < C::DK; ++kk) {
         u32x4 a;
         if (D <= 128 && kt == 0) a = fr[kt][kk];
-        else a = *(const u32x4*)(kbuf + k_lane_off + 32 * kt * C::KROWB + (((2 * kk + h) ^ kswz) << 4));
+        else a = *(const u32x4*)(kbuf + k_lane_off + 32 * kt * C::KROWB + (((2 * kk + h) ^ ksw) << 4));
         z = mfma_qk<DT>(a, qf[kk], z);
       }
       s[kt] = z;
@@ -568,16 +570,18 @@ void attn_fwd_kernel(Params p) {
     if (t + 2 < ntiles) dma_k(key_begin + (t + 2) * BN, kb_dma);
     if (t + 1 < ntiles) dma_v(key_begin + (t + 1) * BN, vb_dma);
     const bool has_next = t + 1 < ntiles;
+    int ksw = kswz;
+    if (!fast) asm volatile("" : "+v"(ksw));
     bool live_n[C::KT], masked_n[C::KT];
     u32x4 fr[C::KT][C::DK];
     if (has_next) {
       tile_flags(t + 1, fast || t + 1 < nfull, live_n, masked_n);
-      k_frags(fr, kb_nxt, live_n);             // K(t+1) reads, in flight during the max below
+      k_frags(fr, kb_nxt, live_n, ksw);        // K(t+1) reads, in flight during the max below
     }
     bool live[C::KT], masked[C::KT];
     tile_flags(t, fast || t < nfull, live, masked);
     softmax_max(t, s_cur, live, masked);       // VALU: mask, row max, rescale
-    if (has_next) scores(s_nxt, fr, kb_nxt, live_n);   // MFMA: S(t+1) ...
+    if (has_next) scores(s_nxt, fr, kb_nxt, live_n, ksw);   // MFMA: S(t+1) ...
     u32x4 pk[KW / 16];
     softmax_exp(s_cur, pk, live);              // ... while the VALU exponentiates P(t)
     pv(s_cur, pk, vb_cur, live);               // MFMA: O += P(t) V(t)
@@ -619,8 +623,8 @@ void attn_fwd_kernel(Params p) {
     bool live0[C::KT], masked0[C::KT];
     tile_flags(0, 0 < nfull, live0, masked0);
     u32x4 fr0[C::KT][C::DK];
-    k_frags(fr0, lk0, live0);
-    scores(sA, fr0, lk0, live0);
+    k_frags(fr0, lk0, live0, kswz);
+    scores(sA, fr0, lk0, live0, kswz);
   }
   int t = 0;
   // Unmasked iterations (tiles t and t+1 both unmasked) in pairs with fixed buffers.
@@ -665,13 +669,13 @@ hipError_t launch(const Params& p0, hipStream_t stream) {
   Params p = p0;
   p.n_qblocks = (p.L + C::BM - 1) / C::BM;
   const long long blocks = (long long)p.n_qblocks * p.bh;
-  // causal head groups: the largest divisor of the heads per XCD whose K/V fits in 8 MiB
+  // causal head groups: the largest divisor of the heads per XCD whose K/V fits the 4 MiB L2
   p.group = 1;
   if (MODE == kMaskCausal && p.bh % 8 == 0) {
     const long long head_kv = (long long)p.L * D * (2 + C::VB);
     const int hx = p.bh / 8;
     for (int g = hx; g >= 1; --g)
-      if (hx % g == 0 && g * head_kv <= (8ll << 20)) {
+      if (hx % g == 0 && g * head_kv <= (4ll << 20)) {
         p.group = g;
         break;
       }

@@ -614,6 +614,37 @@ void attn_fwd_kernel(Params p) {
         }
       }
     }
+    if constexpr (D == 256 && MODE != kMaskBlock) {
+      if (fast && has_next) {
+        // D = 256 runs one wave per SIMD, so nothing hides an LDS read issued right before its
+        // MFMA.  Issue order: four K reads, then one K read after each score MFMA (reads stay
+        // four MFMAs ahead), half of the V^T reads after the last four score MFMAs and the rest
+        // after the first P.V MFMAs, with the exponentials spread over the score MFMAs.
+        constexpr int NS = C::KT * C::DK;
+        constexpr int RPP = C::V8 ? 4 : 2;                          // V^T reads per P.V MFMA
+        constexpr int NP = C::V8 ? (KW / 64) * C::DTL : (KW / 16) * C::DTL;
+        constexpr int NV = NP * RPP, NVE = NV / 2, KA = 4;
+        static_assert(NVE % KA == 0 && (NV - NVE) % RPP == 0, "V^T reads split evenly");
+        __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);
+#pragma unroll
+        for (int i = 0; i < NS - KA; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < KA; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, NVE / KA, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < (NV - NVE) / RPP; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, RPP, 0);
+        }
+      }
+    }
   };
 
   f32x16 sA[C::KT], sB[C::KT];
@@ -736,15 +767,10 @@ attn_status_t validate(const Problem& pr) {
 
 template <int D, int DT>
 hipError_t dispatch_dense(int mode, const Params& p, hipStream_t s) {
-  // D = 64: 8 waves (256 query rows per workgroup, half the K/V streaming per query); D = 128
-  // and 256: 4 waves.  64-key tiles throughout (register budget of two waves per SIMD).
-  if constexpr (D == 64) {
-    if (mode == kMaskCausal) return launch<D, DT, kMaskCausal, 8, 64>(p, s);
-    return launch<D, DT, kMaskNone, 8, 64>(p, s);
-  } else {
-    if (mode == kMaskCausal) return launch<D, DT, kMaskCausal, 4, 64>(p, s);
-    return launch<D, DT, kMaskNone, 4, 64>(p, s);
-  }
+  // 4 waves (128 query rows) per workgroup and 64-key tiles for every head dim: two waves per
+  // SIMD fit the register budget, two workgroups per CU interleave their MFMA and VALU phases.
+  if (mode == kMaskCausal) return launch<D, DT, kMaskCausal, 4, 64>(p, s);
+  return launch<D, DT, kMaskNone, 4, 64>(p, s);
 }
 
 template <int D, int DT>

@@ -212,7 +212,11 @@ def test_deterministic(mode, D, dtype, bs):
 
 @pytest.mark.parametrize("mode,D,dtype,bs,L", [("causal", 128, "bf16", 0, 300), ("none", 64, "f16", 0, 129),
                                                ("block_diag", 128, "f16", 64, 256),
-                                               ("causal", 256, "bf16_v_e5m2", 0, 200)])
+                                               ("causal", 256, "bf16_v_e5m2", 0, 200),
+                                               ("none", 128, "bf16", 0, 257), ("causal", 64, "f16", 0, 193),
+                                               ("none", 256, "f16", 0, 130), ("causal", 256, "bf16", 0, 321),
+                                               ("block_diag", 64, "bf16", 32, 224),
+                                               ("block_diag", 128, "bf16", 128, 384)])
 def test_lse_output(mode, D, dtype, bs, L):
     q, k, v = gpu_qkv(2, 2, L, D, dtype, seed=4)
     o, lse = run(q, k, v, mode, bs, default_scale(D), lse=True)
@@ -224,14 +228,18 @@ def test_lse_output(mode, D, dtype, bs, L):
     assert err <= 1e-4
 
 
-@pytest.mark.parametrize("B,H,L,D,dtype,mode", [
-    (4, 32, 4096, 128, "bf16", "causal"),   # 16 heads per XCD, longest-first head groups
-    (2, 8, 1024, 64, "f16", "causal"),
-    (1, 8, 600, 128, "bf16", "causal"),
-    (3, 5, 300, 64, "f16", "causal"),       # batch*heads not a multiple of 8
-    (2, 8, 1000, 128, "f16", "none"),
+@pytest.mark.parametrize("B,H,L,D,dtype,mode,bs", [
+    (4, 32, 4096, 128, "bf16", "causal", 0),   # 16 heads per XCD, longest-first head groups
+    (2, 8, 1024, 64, "f16", "causal", 0),
+    (1, 8, 600, 128, "bf16", "causal", 0),
+    (3, 5, 300, 64, "f16", "causal", 0),       # batch*heads not a multiple of 8
+    (2, 8, 1000, 128, "f16", "none", 0),
+    (1, 8, 1000, 256, "bf16", "causal", 0),
+    (2, 4, 700, 256, "f16", "none", 0),
+    (2, 8, 1024, 128, "f16", "block_diag", 64),
+    (3, 4, 96, 64, "bf16", "block_diag", 32),
 ])
-def test_every_query_block_of_every_head_written(B, H, L, D, dtype, mode):
+def test_every_query_block_of_every_head_written(B, H, L, D, dtype, mode, bs):
     # V is constant over keys within a head, with a value naming the head: every output row of
     # head (b, h) is then exactly that value (weights summing to one times a constant), whatever
     # the mask.  The output starts as NaN, so a block that is never written, or written with
@@ -241,7 +249,7 @@ def test_every_query_block_of_every_head_written(B, H, L, D, dtype, mode):
     val = (1.0 + torch.arange(B * H, dtype=torch.float32).reshape(B, H, 1, 1)) / 64.0
     v = val.expand(B, H, L, D).to(tdt).contiguous().cuda()
     out = torch.full((B, H, L, D), float("nan"), dtype=tdt, device="cuda")
-    binding.attn_fwd(q, k, v, mask=mode, out=out)
+    binding.attn_fwd(q, k, v, mask=mode, block_size=bs, out=out)
     torch.cuda.synchronize()
     want = val.expand(B, H, L, D).to(tdt).cuda()
     bad = (out != want)

@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 MASK_MODES = {"none": 0, "causal": 1, "block_diag": 2}
-DTYPE_CODES = {"f16": 0, "bf16": 1, "bf16_v_e5m2": 2}
+DTYPE_CODES = {"f16": 0, "bf16": 1, "bf16_v_e5m2": 2, "f16_v_e5m2": 3}
 
 
 class Status:
@@ -78,8 +78,11 @@ def attn_fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, batch, heads, L, D, sm_scale, mask,
 
 def _dtype_code(q, k, v):
     import torch
-    if q.dtype == torch.float16 and k.dtype == torch.float16 and v.dtype == torch.float16:
-        return "f16"
+    if q.dtype == torch.float16 and k.dtype == torch.float16:
+        if v.dtype == torch.float16:
+            return "f16"
+        if v.dtype == torch.float8_e5m2:
+            return "f16_v_e5m2"
     if q.dtype == torch.bfloat16 and k.dtype == torch.bfloat16:
         if v.dtype == torch.bfloat16:
             return "bf16"

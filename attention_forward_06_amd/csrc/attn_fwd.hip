@@ -53,7 +53,7 @@ typedef _Float16 f16x8 __attribute__((__vector_size__(16)));
 typedef float f32x16 __attribute__((__vector_size__(64)));
 
 constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskBlock = 2;
-constexpr int kF16 = 0, kBF16 = 1, kBF16V8 = 2;
+constexpr int kF16 = 0, kBF16 = 1, kBF16V8 = 2, kF16V8 = 3;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
@@ -135,7 +135,8 @@ struct Cfg {
   static constexpr int KT = KW / 32;          // 32-key subtiles a wave computes per tile
   static constexpr int DK = D / 16;           // 16-wide d chunks of Q.K
   static constexpr int DTL = D / 32;          // 32-wide d tiles of O
-  static constexpr bool V8 = (DT == kBF16V8);
+  static constexpr bool V8 = (DT == kBF16V8 || DT == kF16V8);
+  static constexpr int QK = (DT == kF16 || DT == kF16V8) ? kF16 : kBF16;   // Q, K and O element type
   static constexpr int VB = V8 ? 1 : 2;       // bytes per V element
   static constexpr int KROWB = D * 2;         // bytes per K row in LDS (no padding: XOR swizzle)
   static constexpr int VROWB = D * VB;        // bytes per V row in LDS
@@ -418,7 +419,7 @@ void attn_fwd_kernel(Params p) {
         u32x4 a;
         if (D <= 128 && kt == 0) a = fr[kt][kk];
         else a = *(const u32x4*)(kbuf + k_lane_off + 32 * kt * C::KROWB + (((2 * kk + h) ^ ksw) << 4));
-        z = mfma_qk<DT>(a, qf[kk], z);
+        z = mfma_qk<C::QK>(a, qf[kk], z);
       }
       s[kt] = z;
     }
@@ -682,8 +683,8 @@ void attn_fwd_kernel(Params p) {
       for (int a4 = 0; a4 < 4; ++a4) {
         // registers 4*a4 .. 4*a4+3 hold d = 32*dt + 8*a4 + 4*h + 0..3
         u32x2 w;
-        w[0] = pack2<DT == kF16 ? kF16 : kBF16>(acc[dt][4 * a4] * inv, acc[dt][4 * a4 + 1] * inv);
-        w[1] = pack2<DT == kF16 ? kF16 : kBF16>(acc[dt][4 * a4 + 2] * inv, acc[dt][4 * a4 + 3] * inv);
+        w[0] = pack2<C::QK>(acc[dt][4 * a4] * inv, acc[dt][4 * a4 + 1] * inv);
+        w[1] = pack2<C::QK>(acc[dt][4 * a4 + 2] * inv, acc[dt][4 * a4 + 3] * inv);
         *(u32x2*)(orow + (32 * dt + 8 * a4 + 4 * h) * 2) = w;
       }
     if (LSE && h == 0) p.lse[(size_t)bh * L + my_q] = (m_ref + __builtin_amdgcn_logf(l_exact)) * kLn2;
@@ -741,7 +742,7 @@ bool supported(const Problem& pr) {
 }
 
 attn_status_t validate(const Problem& pr) {
-  if (pr.mode < 0 || pr.mode > 2 || pr.dtype < 0 || pr.dtype > 2) return ATTN_ERR_ARG;
+  if (pr.mode < 0 || pr.mode > 2 || pr.dtype < 0 || pr.dtype > 3) return ATTN_ERR_ARG;
   // finite and positive, checked on the bits (independent of floating-point flags)
   const uint32_t sbits = __builtin_bit_cast(uint32_t, pr.sm_scale);
   const bool not_finite = ((sbits >> 23) & 0xffu) == 0xffu;
@@ -800,6 +801,7 @@ hipError_t dispatch(const Problem& pr, const Params& p, hipStream_t s) {
     default:
       if (pr.dtype == kF16) return dispatch_dense<256, kF16>(pr.mode, p, s);
       if (pr.dtype == kBF16) return dispatch_dense<256, kBF16>(pr.mode, p, s);
+      if (pr.dtype == kF16V8) return dispatch_dense<256, kF16V8>(pr.mode, p, s);
       return dispatch_dense<256, kBF16V8>(pr.mode, p, s);
   }
 }

@@ -14,7 +14,7 @@ import math
 
 import torch
 
-DTYPES = ("f16", "bf16", "bf16_v_e5m2")
+DTYPES = ("f16", "bf16", "bf16_v_e5m2", "f16_v_e5m2")
 
 # The five workloads of the target, named by what they are.
 WORKLOADS = {
@@ -30,6 +30,9 @@ WORKLOADS = {
         dict(mode="block_diag", B=8, H=32, L=16384, D=128, dtype="f16", block_size=128),
     "causal_b1_h16_l32768_d256_bf16_ve5m2":
         dict(mode="causal", B=1, H=16, L=32768, D=256, dtype="bf16_v_e5m2", block_size=0),
+    # the fp8-V variant with fp16 Q/K/O (the fp8 branch keys only on V's type)
+    "causal_b1_h16_l32768_d256_f16_ve5m2":
+        dict(mode="causal", B=1, H=16, L=32768, D=256, dtype="f16_v_e5m2", block_size=0),
 }
 
 # The non-causal test matrix of the fused-attention page: (Z, H, N_CTX, HEAD_DIM,
@@ -53,6 +56,8 @@ def storage_dtypes(dtype):
         return torch.bfloat16, torch.bfloat16, torch.bfloat16
     if dtype == "bf16_v_e5m2":
         return torch.bfloat16, torch.bfloat16, torch.float8_e5m2
+    if dtype == "f16_v_e5m2":
+        return torch.float16, torch.float16, torch.float8_e5m2
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

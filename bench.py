@@ -108,7 +108,7 @@ def time_workload(name, steps, warmup):
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) for a, b in evs)
     flops = oracle.attn_flops(w["mode"], B, H, L, D, w["block_size"])
-    vb = 1 if w["dtype"] == "bf16_v_e5m2" else 2
+    vb = 1 if w["dtype"].endswith("_v_e5m2") else 2
     nbytes = B * H * L * D * (2 + 2 + vb + 2)
     ms = total_ms / steps
     del q, k, v, o
@@ -178,12 +178,12 @@ def main():
         copy_calibration()
     names = [HEADLINE, "blockdiag_b8_h32_n16384_d128_bs64_f16",
              "blockdiag_b8_h32_n16384_d128_bs128_f16", "dense_b4_h16_l2048_d64_f16",
-             "causal_b1_h16_l32768_d256_bf16_ve5m2"]
+             "causal_b1_h16_l32768_d256_bf16_ve5m2", "causal_b1_h16_l32768_d256_f16_ve5m2"]
     if a.only:
         names = [a.only]
     res = {}
     for n in names:
-        steps = a.steps if n != "causal_b1_h16_l32768_d256_bf16_ve5m2" else max(1, a.steps // 10)
+        steps = a.steps if "l32768" not in n else max(1, a.steps // 10)
         res[n] = time_workload(n, steps, min(a.warmup, steps))
         print(f"# {n}: {res[n]['ms']:.4f} ms/launch  {res[n]['tflops']:.1f} TFLOP/s  "
               f"{res[n]['gbs']:.1f} GB/s", file=sys.stderr, flush=True)

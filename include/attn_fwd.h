@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
     ATTN_MASK_NONE = 0,
@@ -53,9 +53,11 @@ typedef enum {
 typedef enum {
     ATTN_F16 = 0,          /* Q, K, V, O binary16; P rounded to binary16 before P.V          */
     ATTN_BF16 = 1,         /* Q, K, V, O bfloat16; P rounded to bfloat16 before P.V          */
-    ATTN_BF16_V_E5M2 = 2   /* Q, K, O bfloat16; V OCP fp8 e5m2; P rounded to e5m2 before P.V
+    ATTN_BF16_V_E5M2 = 2,  /* Q, K, O bfloat16; V OCP fp8 e5m2; P rounded to e5m2 before P.V
                               and the row sum taken over the unrounded P ("Fused Attention",
                               _attn_fwd_inner, fp8 branch)                                   */
+    ATTN_F16_V_E5M2 = 3    /* the same with Q, K, O binary16 (the fp8 branch keys only on V's
+                              type)                                                          */
 } attn_dtype_t;
 
 typedef enum {
@@ -82,7 +84,7 @@ typedef enum {
  *
  * Supported set (everything else returns ATTN_ERR_UNSUPPORTED):
  *   none, causal   D in {64, 128}: ATTN_F16, ATTN_BF16; any L >= 1 (a ragged last tile is masked)
- *                  D = 256: ATTN_F16, ATTN_BF16, ATTN_BF16_V_E5M2
+ *                  D = 256: ATTN_F16, ATTN_BF16, ATTN_BF16_V_E5M2, ATTN_F16_V_E5M2
  *   block_diag     D in {64, 128}: ATTN_F16, ATTN_BF16; block_size in {32, 64, 128}
  */
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o,

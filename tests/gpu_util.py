@@ -6,7 +6,8 @@ from attention_forward_06_amd import binding
 from attention_forward_06_amd.inputs import make_qkv
 
 # Max-abs-error tolerances by storage dtype (fp16, bf16, fp8 V/P).
-TOL = {"f16": 2e-3, "bf16": 1e-2, "bf16_v_e5m2": 5e-2}
+TOL = {"f16": 2e-3, "bf16": 1e-2, "bf16_v_e5m2": 5e-2, "f16_v_e5m2": 5e-2}
+V8_DTYPES = ("bf16_v_e5m2", "f16_v_e5m2")
 
 
 def to_f64(t):

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
 
 NONE, CAUSAL, BLOCK = 0, 1, 2
-F16, BF16, V8 = 0, 1, 2
+F16, BF16, V8, F16V8 = 0, 1, 2, 3
 FAKE = 0x1000   # never dereferenced: every call below fails validation or is a no-op
 
 
@@ -40,9 +40,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     with open(HEADER) as f:
-        assert "#define ATTN_ABI_VERSION 1" in f.read()
+        assert "#define ATTN_ABI_VERSION 2" in f.read()
     seen = set()
     for code in range(6):
         s = binding.status_str(code)
@@ -80,13 +80,16 @@ def test_null_pointers(lib, which):
     (dict(D=512), binding.Status.ERR_UNSUPPORTED),
     (dict(D=64, dt=V8), binding.Status.ERR_UNSUPPORTED),
     (dict(D=128, dt=V8), binding.Status.ERR_UNSUPPORTED),
+    (dict(D=128, dt=F16V8), binding.Status.ERR_UNSUPPORTED),
+    (dict(mode=BLOCK, bs=64, dt=F16V8), binding.Status.ERR_UNSUPPORTED),
     (dict(mode=BLOCK, bs=256, L=512), binding.Status.ERR_UNSUPPORTED),
     (dict(mode=BLOCK, bs=16, L=64), binding.Status.ERR_UNSUPPORTED),
     (dict(mode=BLOCK, bs=64, D=256, dt=BF16), binding.Status.ERR_UNSUPPORTED),
     (dict(mode=BLOCK, bs=64, dt=V8), binding.Status.ERR_UNSUPPORTED),
     (dict(mode=3), binding.Status.ERR_ARG),
     (dict(mode=-1), binding.Status.ERR_ARG),
-    (dict(dt=3), binding.Status.ERR_ARG),
+    (dict(dt=4), binding.Status.ERR_ARG),
+    (dict(dt=-1), binding.Status.ERR_ARG),
     (dict(scale=float("nan")), binding.Status.ERR_ARG),
     (dict(scale=float("inf")), binding.Status.ERR_ARG),
     (dict(scale=0.0), binding.Status.ERR_ARG),
@@ -111,6 +114,7 @@ def test_empty_problem_is_a_noop(lib, args):
 @pytest.mark.parametrize("mode,D,dt,bs", [
     (NONE, 64, F16, 0), (NONE, 128, BF16, 0), (CAUSAL, 64, BF16, 0), (CAUSAL, 128, F16, 0),
     (NONE, 256, F16, 0), (CAUSAL, 256, BF16, 0), (CAUSAL, 256, V8, 0), (NONE, 256, V8, 0),
+    (CAUSAL, 256, F16V8, 0), (NONE, 256, F16V8, 0),
     (BLOCK, 128, F16, 64), (BLOCK, 128, BF16, 128), (BLOCK, 64, F16, 32), (BLOCK, 64, BF16, 128),
 ])
 def test_supported_set(lib, mode, D, dt, bs):

@@ -14,7 +14,7 @@ import oracle
 from attention_forward_06_amd import binding
 from attention_forward_06_amd.inputs import WORKLOADS, FUSED_PAGE_MATRIX, make_qkv, default_scale
 
-from gpu_util import TOL, gpu_qkv, run, sample_rows, to_f64
+from gpu_util import TOL, V8_DTYPES, gpu_qkv, run, sample_rows, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,7 @@ def _check(q, k, v, mode, bs, scale, dtype, tag, rows=None, heads=None):
     qn, kn, vn, on = (to_f64(x) for x in (q, k, v, o))
     if heads is not None:
         qn, kn, vn, on = (x[heads[0]:heads[0] + 1, heads[1]:heads[1] + 1] for x in (qn, kn, vn, on))
-    p_round = "e5m2" if dtype == "bf16_v_e5m2" else None
+    p_round = "e5m2" if dtype in V8_DTYPES else None
     ref = oracle.attn_ref(qn, kn, vn, mode, scale, bs, rows=rows, p_round=p_round)
     got = on if rows is None else on[:, :, rows]
     assert np.all(np.isfinite(got)), f"{tag}: non-finite output"
@@ -41,7 +41,9 @@ def _check(q, k, v, mode, bs, scale, dtype, tag, rows=None, heads=None):
 # ------------------------------------------------------------------ small shapes, all instances
 DENSE_CASES = [(mode, D, dt) for mode in ("none", "causal") for D in (64, 128, 256)
                for dt in ("f16", "bf16")] + [("none", 256, "bf16_v_e5m2"),
-                                             ("causal", 256, "bf16_v_e5m2")]
+                                             ("causal", 256, "bf16_v_e5m2"),
+                                             ("none", 256, "f16_v_e5m2"),
+                                             ("causal", 256, "f16_v_e5m2")]
 
 
 @pytest.mark.parametrize("mode,D,dtype", DENSE_CASES)
@@ -61,16 +63,17 @@ def test_block_diag_small(D, dtype, bs, nblk):
     _check(q, k, v, "block_diag", bs, default_scale(D), dtype, f"block bs{bs} D{D} {dtype} L{L}")
 
 
-def test_fp8_matches_online_frame_tightly():
+@pytest.mark.parametrize("dtype", V8_DTYPES)
+def test_fp8_matches_online_frame_tightly(dtype):
     # The kernel rounds P to e5m2 against the running max of 64-key tiles, as the pages'
     # recurrence does; the fp64 recurrence with the same tile width agrees far inside 5e-2.
     D, L = 256, 384
-    q, k, v = gpu_qkv(1, 2, L, D, "bf16_v_e5m2", seed=5)
+    q, k, v = gpu_qkv(1, 2, L, D, dtype, seed=5)
     o = run(q, k, v, "causal", 0, default_scale(D))
     ref = oracle.attn_online_ref(to_f64(q), to_f64(k), to_f64(v), "causal", default_scale(D), 64,
                                  p_round="e5m2")
     err = float(np.abs(to_f64(o) - ref).max())
-    _report("fp8 causal vs online-frame oracle", err, 1e-2)
+    _report(f"fp8 causal {dtype} vs online-frame oracle", err, 1e-2)
     assert err <= 1e-2
 
 
@@ -84,7 +87,7 @@ def test_workload_full_size(name):
     scale = default_scale(D)
     o = run(q, k, v, mode, bs, scale)
     assert torch.isfinite(o.float()).all()
-    p_round = "e5m2" if dt == "bf16_v_e5m2" else None
+    p_round = "e5m2" if dt in V8_DTYPES else None
     heads = [(0, 0), (B - 1, H - 1), (B // 2, H // 3)]
     rows = sample_rows(L, n_edge=64 if L > 8192 else 128, n_rand=128)
     worst = 0.0
@@ -125,7 +128,8 @@ def test_fused_page_matrix(Z, H, N, D, dtype, BM, BN):
 
 
 # ------------------------------------------------------------------ invariants on the GPU
-@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16"), (256, "bf16"), (256, "bf16_v_e5m2")])
+@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16"), (256, "bf16"), (256, "bf16_v_e5m2"),
+                                     (256, "f16_v_e5m2")])
 def test_causal_row0_is_v0_bit_exact(D, dtype):
     q, k, v = gpu_qkv(2, 3, 200, D, dtype, seed=3, std=3.0)
     o = run(q, k, v, "causal", 0, default_scale(D))
@@ -213,6 +217,7 @@ def test_deterministic(mode, D, dtype, bs):
 @pytest.mark.parametrize("mode,D,dtype,bs,L", [("causal", 128, "bf16", 0, 300), ("none", 64, "f16", 0, 129),
                                                ("block_diag", 128, "f16", 64, 256),
                                                ("causal", 256, "bf16_v_e5m2", 0, 200),
+                                               ("none", 256, "f16_v_e5m2", 0, 150),
                                                ("none", 128, "bf16", 0, 257), ("causal", 64, "f16", 0, 193),
                                                ("none", 256, "f16", 0, 130), ("causal", 256, "bf16", 0, 321),
                                                ("block_diag", 64, "bf16", 32, 224),

@@ -133,13 +133,18 @@ struct Cfg {
   // KW: keys one wave works on per tile.  KW = BN except for block_diag with blocks smaller
   // than the tile, where each wave only touches its own diagonal block inside the tile.
   static constexpr int KT = KW / 32;          // 32-key subtiles a wave computes per tile
-  static constexpr int DK = D / 16;           // 16-wide d chunks of Q.K
-  static constexpr int DTL = D / 32;          // 32-wide d tiles of O
+  // Tile head dim: D = 16 runs as 32, with the upper half of every Q, K and V row zero (the DMA
+  // and the Q loads fill it with zeros; the epilogue stores only d < D).
+  static constexpr int DP = D < 32 ? 32 : D;
+  static constexpr int DK = DP / 16;          // 16-wide d chunks of Q.K
+  static constexpr int DTL = DP / 32;         // 32-wide d tiles of O
   static constexpr bool V8 = (DT == kBF16V8 || DT == kF16V8);
   static constexpr int QK = (DT == kF16 || DT == kF16V8) ? kF16 : kBF16;   // Q, K and O element type
   static constexpr int VB = V8 ? 1 : 2;       // bytes per V element
-  static constexpr int KROWB = D * 2;         // bytes per K row in LDS (no padding: XOR swizzle)
-  static constexpr int VROWB = D * VB;        // bytes per V row in LDS
+  static constexpr int KROWB = DP * 2;        // bytes per K row in LDS (no padding: XOR swizzle)
+  static constexpr int VROWB = DP * VB;       // bytes per V row in LDS
+  static constexpr int KGROWB = D * 2;        // bytes per K row in HBM
+  static constexpr int VGROWB = D * VB;       // bytes per V row in HBM
   static constexpr int KTILE = BN * KROWB;
   static constexpr int VTILE = BN * VROWB;
   static constexpr int NBUF = MODE == kMaskBlock ? 1 : 2;   // double-buffer the streamed tiles
@@ -171,22 +176,27 @@ struct Cfg {
   static_assert(!V8 || BN % 64 == 0, "fp8 P.V consumes 64 keys per MFMA");
   static_assert(KTILE % (1024 * NW) == 0 && VTILE % (1024 * NW) == 0,
                 "tiles split into whole 1 KiB DMA instructions per wave");
-  static_assert(D % 32 == 0, "head dim is a multiple of 32");
+  static_assert(DP % 32 == 0 && (D == DP || D == 16), "head dim 16 or a multiple of 32");
 };
 
 // XOR swizzles of the 16-byte chunks inside a tile row (LDS-DMA writes rows unpadded).
-// K: the 16 lanes of a ds_read_b128 read the same chunk of 16 different rows -> spread rows
-//    over 16 distinct chunk positions of a 256-byte bank window.
+// K: the 16 lanes of a ds_read_b128 read the same chunk of 16 different rows (rows 0..15 up to
+//    the bit swap pi) -> spread them over 16 distinct chunk positions of a 256-byte bank window:
+//    a row of ROWB bytes holds ROWB/16 chunks, 256/ROWB rows share a window, and the XOR takes
+//    the row bits above those.
 // V (16-bit): a ds_read_b64_tr_b16 half-wave reads 4 rows x 64 contiguous bytes -> give the
-//    4 rows disjoint 64-byte slots.   V (fp8): tr_b8 reads 8 rows x 32 bytes -> 8 slots of 32.
+//    4 rows disjoint 64-byte slots (64-byte rows already are).   V (fp8): tr_b8 reads 8 rows x
+//    32 bytes -> 8 slots of 32.
 template <int ROWB>
 __device__ __forceinline__ int swz_k(int r) {
-  if constexpr (ROWB == 128) return (r >> 1) & 7;
+  if constexpr (ROWB == 64) return (r >> 2) & 3;
+  else if constexpr (ROWB == 128) return (r >> 1) & 7;
   else return r & 15;
 }
 template <int ROWB, bool V8>
 __device__ __forceinline__ int swz_v(int r) {
   if constexpr (V8) return 2 * (r & 7);
+  else if constexpr (ROWB == 64) return 0;
   else if constexpr (ROWB == 128) return 4 * ((r >> 1) & 1);
   else return 4 * (r & 3);
 }
@@ -229,14 +239,15 @@ __device__ __forceinline__ float partner(float x) {
 // the same code written as a lambda inside the kernel made the host compiler drop the kernel's
 // launch stub.
 // inside: the caller knows the whole tile lies below row L (no per-row check).
-template <int ROWB, int NI, int PER, int NW, int BN>
+template <int ROWB, int GROWB, int NI, int PER, int NW, int BN>
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, int key0, int L, int wave, int lane,
                                          unsigned oob, const unsigned* off, unsigned char* buf,
                                          const bool inside) {
+  constexpr int RPI = NW * 1024 / ROWB;              // tile rows one instruction index covers
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     auto* dst = (__attribute__((address_space(3))) void*)(buf + (wave + i * NW) * 1024);
-    const int soff = key0 * ROWB + i * NW * 1024;    // scalar part of the offset
+    const int soff = (key0 + i * RPI) * GROWB;       // scalar part of the offset
     if (inside) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off[i % PER], soff, 0, 0);
     } else {
@@ -283,34 +294,37 @@ void attn_fwd_kernel(Params p) {
 
   // HBM -> LDS by DMA: instruction j of a tile fills LDS bytes [1024 j, 1024 j + 1024); lane l
   // lands at +16 l.  The lane fetches the global chunk that the swizzle stores at that slot.
-  // Per lane the tile-relative row and byte offset of every instruction are fixed; a tile adds
-  // key0 * row_bytes as a scalar offset.  Tiles reaching past row L take the checked path, where
-  // rows at or past L read as zeros.
-  // The lane's offset inside instruction i repeats with period KPER (VPER) in i, up to the
-  // 1 KiB-per-instruction stride: the swizzle only looks at low row bits.
+  // Per lane the row within the instruction's block of rows and the chunk are fixed; instruction
+  // index i and the tile add (key0 + i * rows per index) * row_bytes as a scalar offset.  Tiles
+  // reaching past row L take the checked path, where rows at or past L read as zeros; so do the
+  // chunks of a padded row (D = 16), whose offset is past any buffer.
+  // The lane's chunk repeats with period KPER (VPER) in i: the swizzle only looks at low row bits.
+  constexpr unsigned kPadOff = 0x80000000u;
   unsigned k_off[C::KPER], v_off[C::VPER];
 #pragma unroll
   for (int i = 0; i < C::KPER; ++i) {
     const int byte = (wave + i * NW) * 1024 + lane * 16;
     const int row = byte / C::KROWB;
-    k_off[i] = (unsigned)(row * C::KROWB + ((((byte % C::KROWB) >> 4) ^ swz_k<C::KROWB>(row)) << 4)) -
-               (unsigned)(i * NW * 1024);
+    const int lch = ((byte % C::KROWB) >> 4) ^ swz_k<C::KROWB>(row);   // chunk stored at this slot
+    const int rin = (wave * 1024 + lane * 16) / C::KROWB;               // row - i * rows per index
+    k_off[i] = lch * 16 < C::KGROWB ? (unsigned)(rin * C::KGROWB + lch * 16) : kPadOff;
   }
 #pragma unroll
   for (int i = 0; i < C::VPER; ++i) {
     const int byte = (wave + i * NW) * 1024 + lane * 16;
     const int row = byte / C::VROWB;
-    v_off[i] = (unsigned)(row * C::VROWB + ((((byte % C::VROWB) >> 4) ^ swz_v<C::VROWB, C::V8>(row)) << 4)) -
-               (unsigned)(i * NW * 1024);
+    const int lch = ((byte % C::VROWB) >> 4) ^ swz_v<C::VROWB, C::V8>(row);
+    const int rin = (wave * 1024 + lane * 16) / C::VROWB;
+    v_off[i] = lch * 16 < C::VGROWB ? (unsigned)(rin * C::VGROWB + lch * 16) : kPadOff;
   }
   // One scalar branch per tile selects the unchecked copy when no row of the tile is past L.
   auto dma_k = [&](int key0, unsigned char* kb) __attribute__((always_inline)) {
-    if (key0 + BN <= L) dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb, true);
-    else dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb, false);
+    if (key0 + BN <= L) dma_rows<C::KROWB, C::KGROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb, true);
+    else dma_rows<C::KROWB, C::KGROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb, false);
   };
   auto dma_v = [&](int key0, unsigned char* vb) __attribute__((always_inline)) {
-    if (key0 + BN <= L) dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, true);
-    else dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, false);
+    if (key0 + BN <= L) dma_rows<C::VROWB, C::VGROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, true);
+    else dma_rows<C::VROWB, C::VGROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, false);
   };
 
   // Key range walked by this workgroup.
@@ -336,7 +350,8 @@ void attn_fwd_kernel(Params p) {
   u32x4 qf[C::DK];
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
-    const unsigned off = (unsigned)(my_q < L ? (my_q * D + 16 * kk + 8 * h) * 2 : head_elems * 2);
+    const bool in = my_q < L && 16 * kk + 8 * h < D;   // d >= D: the zero half of a padded row
+    const unsigned off = (unsigned)(in ? (my_q * D + 16 * kk + 8 * h) * 2 : head_elems * 2);
     qf[kk] = buf_load16(rq, off);
   }
 
@@ -682,6 +697,7 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         // registers 4*a4 .. 4*a4+3 hold d = 32*dt + 8*a4 + 4*h + 0..3
+        if (32 * dt + 8 * a4 >= D) continue;      // padded head dim: nothing to store
         u32x2 w;
         w[0] = pack2<C::QK>(acc[dt][4 * a4] * inv, acc[dt][4 * a4 + 1] * inv);
         w[1] = pack2<C::QK>(acc[dt][4 * a4 + 2] * inv, acc[dt][4 * a4 + 3] * inv);
@@ -732,7 +748,7 @@ struct Problem {
 bool supported(const Problem& pr) {
   const bool dense = pr.mode == kMaskNone || pr.mode == kMaskCausal;
   if (dense) {
-    if (pr.D == 64 || pr.D == 128) return pr.dtype == kF16 || pr.dtype == kBF16;
+    if (pr.D == 16 || pr.D == 32 || pr.D == 64 || pr.D == 128) return pr.dtype == kF16 || pr.dtype == kBF16;
     if (pr.D == 256) return true;
     return false;
   }
@@ -792,6 +808,12 @@ hipError_t dispatch(const Problem& pr, const Params& p, hipStream_t s) {
                             : dispatch_block<128, kBF16>(pr.block_size, p, s);
   }
   switch (pr.D) {
+    case 16:
+      return pr.dtype == kF16 ? dispatch_dense<16, kF16>(pr.mode, p, s)
+                              : dispatch_dense<16, kBF16>(pr.mode, p, s);
+    case 32:
+      return pr.dtype == kF16 ? dispatch_dense<32, kF16>(pr.mode, p, s)
+                              : dispatch_dense<32, kBF16>(pr.mode, p, s);
     case 64:
       return pr.dtype == kF16 ? dispatch_dense<64, kF16>(pr.mode, p, s)
                               : dispatch_dense<64, kBF16>(pr.mode, p, s);

@@ -30,6 +30,11 @@ WORKLOADS = {
         dict(mode="block_diag", B=8, H=32, L=16384, D=128, dtype="f16", block_size=128),
     "causal_b1_h16_l32768_d256_bf16_ve5m2":
         dict(mode="causal", B=1, H=16, L=32768, D=256, dtype="bf16_v_e5m2", block_size=0),
+    # the small head dims the fused-attention page's wrapper also accepts
+    "dense_b4_h16_l2048_d32_f16":
+        dict(mode="none", B=4, H=16, L=2048, D=32, dtype="f16", block_size=0),
+    "causal_b4_h32_l4096_d16_bf16":
+        dict(mode="causal", B=4, H=32, L=4096, D=16, dtype="bf16", block_size=0),
     # the fp8-V variant with fp16 Q/K/O (the fp8 branch keys only on V's type)
     "causal_b1_h16_l32768_d256_f16_ve5m2":
         dict(mode="causal", B=1, H=16, L=32768, D=256, dtype="f16_v_e5m2", block_size=0),

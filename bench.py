@@ -178,7 +178,8 @@ def main():
         copy_calibration()
     names = [HEADLINE, "blockdiag_b8_h32_n16384_d128_bs64_f16",
              "blockdiag_b8_h32_n16384_d128_bs128_f16", "dense_b4_h16_l2048_d64_f16",
-             "causal_b1_h16_l32768_d256_bf16_ve5m2", "causal_b1_h16_l32768_d256_f16_ve5m2"]
+             "causal_b1_h16_l32768_d256_bf16_ve5m2", "causal_b1_h16_l32768_d256_f16_ve5m2",
+             "dense_b4_h16_l2048_d32_f16", "causal_b4_h32_l4096_d16_bf16"]
     if a.only:
         names = [a.only]
     res = {}

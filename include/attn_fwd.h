@@ -83,7 +83,9 @@ typedef enum {
  *   stream       hipStream_t to enqueue on (NULL: default stream).
  *
  * Supported set (everything else returns ATTN_ERR_UNSUPPORTED):
- *   none, causal   D in {64, 128}: ATTN_F16, ATTN_BF16; any L >= 1 (a ragged last tile is masked)
+ *   none, causal   D in {16, 32, 64, 128}: ATTN_F16, ATTN_BF16; any L >= 1 (a ragged last tile is
+ *                  masked).  The page's wrapper accepts head dims 16..256 ("Fused Attention",
+ *                  attention wrapper shape checks).
  *                  D = 256: ATTN_F16, ATTN_BF16, ATTN_BF16_V_E5M2, ATTN_F16_V_E5M2
  *   block_diag     D in {64, 128}: ATTN_F16, ATTN_BF16; block_size in {32, 64, 128}
  */

@@ -76,7 +76,10 @@ def test_null_pointers(lib, which):
     (dict(B=1 << 40, H=1 << 40), binding.Status.ERR_SHAPE),       # product overflows
     (dict(B=1 << 20, H=1 << 12, L=64), binding.Status.ERR_SHAPE), # batch*heads >= 2^31
     (dict(D=96), binding.Status.ERR_UNSUPPORTED),
-    (dict(D=32), binding.Status.ERR_UNSUPPORTED),
+    (dict(D=48), binding.Status.ERR_UNSUPPORTED),
+    (dict(D=8), binding.Status.ERR_UNSUPPORTED),
+    (dict(D=16, dt=V8), binding.Status.ERR_UNSUPPORTED),
+    (dict(mode=BLOCK, bs=64, D=32), binding.Status.ERR_UNSUPPORTED),
     (dict(D=512), binding.Status.ERR_UNSUPPORTED),
     (dict(D=64, dt=V8), binding.Status.ERR_UNSUPPORTED),
     (dict(D=128, dt=V8), binding.Status.ERR_UNSUPPORTED),
@@ -115,6 +118,7 @@ def test_empty_problem_is_a_noop(lib, args):
     (NONE, 64, F16, 0), (NONE, 128, BF16, 0), (CAUSAL, 64, BF16, 0), (CAUSAL, 128, F16, 0),
     (NONE, 256, F16, 0), (CAUSAL, 256, BF16, 0), (CAUSAL, 256, V8, 0), (NONE, 256, V8, 0),
     (CAUSAL, 256, F16V8, 0), (NONE, 256, F16V8, 0),
+    (NONE, 16, F16, 0), (CAUSAL, 16, BF16, 0), (NONE, 32, BF16, 0), (CAUSAL, 32, F16, 0),
     (BLOCK, 128, F16, 64), (BLOCK, 128, BF16, 128), (BLOCK, 64, F16, 32), (BLOCK, 64, BF16, 128),
 ])
 def test_supported_set(lib, mode, D, dt, bs):

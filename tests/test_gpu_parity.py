@@ -39,7 +39,7 @@ def _check(q, k, v, mode, bs, scale, dtype, tag, rows=None, heads=None):
 
 
 # ------------------------------------------------------------------ small shapes, all instances
-DENSE_CASES = [(mode, D, dt) for mode in ("none", "causal") for D in (64, 128, 256)
+DENSE_CASES = [(mode, D, dt) for mode in ("none", "causal") for D in (16, 32, 64, 128, 256)
                for dt in ("f16", "bf16")] + [("none", 256, "bf16_v_e5m2"),
                                              ("causal", 256, "bf16_v_e5m2"),
                                              ("none", 256, "f16_v_e5m2"),
@@ -128,6 +128,15 @@ def test_fused_page_matrix(Z, H, N, D, dtype, BM, BN):
 
 
 # ------------------------------------------------------------------ invariants on the GPU
+@pytest.mark.parametrize("Z,H,N,D,dtype", [(1, 1, 128, 16, "f16"), (2, 2, 256, 16, "bf16"),
+                                           (1, 2, 128, 32, "bf16"), (4, 8, 1024, 32, "f16")])
+def test_fused_page_small_head_dims(Z, H, N, D, dtype):
+    # The fused-attention page's wrapper accepts head dims 16 and 32 besides 64/128/256; its test
+    # recipe (seed 20, N(0, 0.5), sm_scale 0.5, non-causal) at those dims, against the oracle.
+    q, k, v = gpu_qkv(Z, H, N, D, dtype, seed=20, std=0.5)
+    _check(q, k, v, "none", 0, 0.5, dtype, f"fused-page recipe {Z},{H},{N},{D},{dtype}")
+
+
 @pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16"), (256, "bf16"), (256, "bf16_v_e5m2"),
                                      (256, "f16_v_e5m2")])
 def test_causal_row0_is_v0_bit_exact(D, dtype):
@@ -221,7 +230,8 @@ def test_deterministic(mode, D, dtype, bs):
                                                ("none", 128, "bf16", 0, 257), ("causal", 64, "f16", 0, 193),
                                                ("none", 256, "f16", 0, 130), ("causal", 256, "bf16", 0, 321),
                                                ("block_diag", 64, "bf16", 32, 224),
-                                               ("block_diag", 128, "bf16", 128, 384)])
+                                               ("block_diag", 128, "bf16", 128, 384),
+                                               ("causal", 16, "f16", 0, 150), ("none", 32, "bf16", 0, 97)])
 def test_lse_output(mode, D, dtype, bs, L):
     q, k, v = gpu_qkv(2, 2, L, D, dtype, seed=4)
     o, lse = run(q, k, v, mode, bs, default_scale(D), lse=True)
@@ -243,6 +253,8 @@ def test_lse_output(mode, D, dtype, bs, L):
     (2, 4, 700, 256, "f16", "none", 0),
     (2, 8, 1024, 128, "f16", "block_diag", 64),
     (3, 4, 96, 64, "bf16", "block_diag", 32),
+    (2, 8, 777, 16, "f16", "causal", 0),
+    (2, 8, 640, 32, "bf16", "none", 0),
 ])
 def test_every_query_block_of_every_head_written(B, H, L, D, dtype, mode, bs):
     # V is constant over keys within a head, with a value naming the head: every output row of

@@ -45,6 +45,10 @@ def load_library():
     lib.attn_fwd.restype = i32
     lib.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i64, i32, vp]
     lib.attn_fwd_lse.restype = i32
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.attn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64p, i64p, i64p, i64p,
+                                     f32, i32, i64, i32, vp]
+    lib.attn_fwd_strided.restype = i32
     lib.attn_fwd_check.argtypes = [i64, i64, i64, i64, f32, i32, i64, i32]
     lib.attn_fwd_check.restype = i32
     lib.attn_status_str.argtypes = [i32]
@@ -76,6 +80,18 @@ def attn_fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, batch, heads, L, D, sm_scale, mask,
                             DTYPE_CODES[dtype] if isinstance(dtype, str) else dtype, stream_ptr)
 
 
+def attn_fwd_strided_raw(q_ptr, k_ptr, v_ptr, o_ptr, batch, heads, L, D, strides, sm_scale, mask,
+                         block_size, dtype, stream_ptr, lse_ptr=None):
+    """Direct C call for tensors with contiguous D and element strides (batch, head, row) given
+    per tensor in `strides` = (q, k, v, o); returns the status code."""
+    lib = load_library()
+    arrs = [(ctypes.c_int64 * 3)(*[int(x) for x in st]) for st in strides]
+    return lib.attn_fwd_strided(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, batch, heads, L, D, *arrs,
+                                sm_scale, MASK_MODES[mask] if isinstance(mask, str) else mask,
+                                block_size, DTYPE_CODES[dtype] if isinstance(dtype, str) else dtype,
+                                stream_ptr)
+
+
 def _dtype_code(q, k, v):
     import torch
     if q.dtype == torch.float16 and k.dtype == torch.float16:
@@ -94,6 +110,8 @@ def _dtype_code(q, k, v):
 def attn_fwd(q, k, v, mask="none", block_size=0, sm_scale=None, out=None, return_lse=False):
     """Attention forward on [batch, heads, L, D] CUDA(HIP) tensors; returns o (and lse).
 
+    The tensors may be any views whose last dimension is contiguous (for example a
+    [batch, L, heads, D] tensor permuted to [batch, heads, L, D]); o then takes q's layout.
     o has q's dtype; lse is fp32 [batch, heads, L] (natural log of the row normaliser).
     Enqueued on torch's current stream.
     """
@@ -103,10 +121,10 @@ def attn_fwd(q, k, v, mask="none", block_size=0, sm_scale=None, out=None, return
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [batch, heads, L, D]")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D [batch, heads, L, D]")
+        if t.stride(3) != 1 and t.shape[3] > 1:
+            raise ValueError(f"{name} must have a contiguous last (head) dimension")
     if not (q.shape == k.shape == v.shape):
         raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if not (q.device == k.device == v.device):
@@ -117,13 +135,21 @@ def attn_fwd(q, k, v, mask="none", block_size=0, sm_scale=None, out=None, return
         sm_scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+        if out.stride(3) != 1 and D > 1:
+            out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != q.dtype or (out.stride(3) != 1 and D > 1):
+        raise ValueError("out must be shaped and typed like q with a contiguous last dimension")
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, D,
-                      float(sm_scale), mask, block_size, dtype, stream,
-                      lse.data_ptr() if lse is not None else None)
+    lse_ptr = lse.data_ptr() if lse is not None else None
+    if all(t.is_contiguous() for t in (q, k, v, out)):
+        st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, D,
+                          float(sm_scale), mask, block_size, dtype, stream, lse_ptr)
+    else:
+        strides = [t.stride()[:3] for t in (q, k, v, out)]
+        st = attn_fwd_strided_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H,
+                                  L, D, strides, float(sm_scale), mask, block_size, dtype, stream,
+                                  lse_ptr)
     if st != Status.OK:
         raise RuntimeError(f"attn_fwd failed: {status_str(st)} (status {st})")
     return (out, lse) if return_lse else out

@@ -58,12 +58,20 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 
+// Element strides of one [batch, heads, L, D] tensor; D is contiguous.
+struct Layout {
+  long long sb, sh;  // batch, head
+  int sr;            // row (sequence position), >= D
+};
+
 struct Params {
   const unsigned char* q;
   const unsigned char* k;
   const unsigned char* v;
   unsigned char* o;
   float* lse;
+  Layout lq, lk, lv, lo;
+  int heads;
   int L;
   int bh;          // batch * heads
   int n_qblocks;   // query blocks per (batch, head)
@@ -239,20 +247,25 @@ __device__ __forceinline__ float partner(float x) {
 // the same code written as a lambda inside the kernel made the host compiler drop the kernel's
 // launch stub.
 // inside: the caller knows the whole tile lies below row L (no per-row check).
-template <int ROWB, int GROWB, int NI, int PER, int NW, int BN>
-__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, int key0, int L, int wave, int lane,
-                                         unsigned oob, const unsigned* off, unsigned char* buf,
+// rs: bytes between consecutive rows in HBM.
+template <int ROWB, int NI, int PER, int NW, int BN>
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t r, int key0, int L, int rs, int wave,
+                                         int lane, unsigned oob, const unsigned* off, unsigned char* buf,
                                          const bool inside) {
   constexpr int RPI = NW * 1024 / ROWB;              // tile rows one instruction index covers
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     auto* dst = (__attribute__((address_space(3))) void*)(buf + (wave + i * NW) * 1024);
-    const int soff = (key0 + i * RPI) * GROWB;       // scalar part of the offset
+    // Scalar part of the offset, made opaque (readfirstlane of a uniform value): otherwise the
+    // compiler splits off each index's constant row offset times the run-time row stride and
+    // adds it to the lane offset in a separate register per index, held through the loop.
+    const int soff = __builtin_amdgcn_readfirstlane((key0 + i * RPI) * rs);
+    const unsigned vo = off[i % PER];
     if (inside) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off[i % PER], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, vo, soff, 0, 0);
     } else {
       const int row = ((wave + i * NW) * 1024 + lane * 16) / ROWB;
-      const unsigned o = key0 + row < L ? off[i % PER] + (unsigned)soff : oob;
+      const unsigned o = key0 + row < L ? vo + (unsigned)soff : oob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, o, 0, 0, 0);
     }
   }
@@ -283,14 +296,19 @@ void attn_fwd_kernel(Params p) {
   const int qw0 = m0 + 32 * wave;         // first query row of this wave
   const int my_q = qw0 + col;
 
-  const size_t head_elems = (size_t)L * D;
-  const unsigned char* qh = p.q + (size_t)bh * head_elems * 2;
-  const unsigned char* kh = p.k + (size_t)bh * head_elems * 2;
-  const unsigned char* vh = p.v + (size_t)bh * head_elems * C::VB;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, (unsigned)(head_elems * 2));
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, (unsigned)(head_elems * 2));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, (unsigned)(head_elems * C::VB));
-  const unsigned k_oob = (unsigned)(head_elems * 2), v_oob = (unsigned)(head_elems * C::VB);
+  // This head's rows of each tensor: base, row stride, and extent (the buffer resources end at the
+  // last row, so rows at or past L -- and the padding offset -- read as zeros).
+  const int bi = bh / p.heads, hi = bh - bi * p.heads;
+  const unsigned char* qh = p.q + (size_t)(bi * p.lq.sb + hi * p.lq.sh) * 2;
+  const unsigned char* kh = p.k + (size_t)(bi * p.lk.sb + hi * p.lk.sh) * 2;
+  const unsigned char* vh = p.v + (size_t)(bi * p.lv.sb + hi * p.lv.sh) * C::VB;
+  const int q_rs = p.lq.sr * 2, k_rs = p.lk.sr * 2, v_rs = p.lv.sr * C::VB;   // bytes per row
+  const unsigned q_ext = (unsigned)((L - 1) * q_rs + D * 2);
+  const unsigned k_oob = (unsigned)((L - 1) * k_rs + D * 2);
+  const unsigned v_oob = (unsigned)((L - 1) * v_rs + D * C::VB);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh, q_ext);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, k_oob);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, v_oob);
 
   // HBM -> LDS by DMA: instruction j of a tile fills LDS bytes [1024 j, 1024 j + 1024); lane l
   // lands at +16 l.  The lane fetches the global chunk that the swizzle stores at that slot.
@@ -307,7 +325,7 @@ void attn_fwd_kernel(Params p) {
     const int row = byte / C::KROWB;
     const int lch = ((byte % C::KROWB) >> 4) ^ swz_k<C::KROWB>(row);   // chunk stored at this slot
     const int rin = (wave * 1024 + lane * 16) / C::KROWB;               // row - i * rows per index
-    k_off[i] = lch * 16 < C::KGROWB ? (unsigned)(rin * C::KGROWB + lch * 16) : kPadOff;
+    k_off[i] = lch * 16 < C::KGROWB ? (unsigned)(rin * k_rs + lch * 16) : kPadOff;
   }
 #pragma unroll
   for (int i = 0; i < C::VPER; ++i) {
@@ -315,16 +333,16 @@ void attn_fwd_kernel(Params p) {
     const int row = byte / C::VROWB;
     const int lch = ((byte % C::VROWB) >> 4) ^ swz_v<C::VROWB, C::V8>(row);
     const int rin = (wave * 1024 + lane * 16) / C::VROWB;
-    v_off[i] = lch * 16 < C::VGROWB ? (unsigned)(rin * C::VGROWB + lch * 16) : kPadOff;
+    v_off[i] = lch * 16 < C::VGROWB ? (unsigned)(rin * v_rs + lch * 16) : kPadOff;
   }
   // One scalar branch per tile selects the unchecked copy when no row of the tile is past L.
   auto dma_k = [&](int key0, unsigned char* kb) __attribute__((always_inline)) {
-    if (key0 + BN <= L) dma_rows<C::KROWB, C::KGROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb, true);
-    else dma_rows<C::KROWB, C::KGROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, wave, lane, k_oob, k_off, kb, false);
+    if (key0 + BN <= L) dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, k_rs, wave, lane, k_oob, k_off, kb, true);
+    else dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, k_rs, wave, lane, k_oob, k_off, kb, false);
   };
   auto dma_v = [&](int key0, unsigned char* vb) __attribute__((always_inline)) {
-    if (key0 + BN <= L) dma_rows<C::VROWB, C::VGROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, true);
-    else dma_rows<C::VROWB, C::VGROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, wave, lane, v_oob, v_off, vb, false);
+    if (key0 + BN <= L) dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, v_rs, wave, lane, v_oob, v_off, vb, true);
+    else dma_rows<C::VROWB, C::VDMA, C::VPER, NW, BN>(rv, key0, L, v_rs, wave, lane, v_oob, v_off, vb, false);
   };
 
   // Key range walked by this workgroup.
@@ -351,7 +369,7 @@ void attn_fwd_kernel(Params p) {
 #pragma unroll
   for (int kk = 0; kk < C::DK; ++kk) {
     const bool in = my_q < L && 16 * kk + 8 * h < D;   // d >= D: the zero half of a padded row
-    const unsigned off = (unsigned)(in ? (my_q * D + 16 * kk + 8 * h) * 2 : head_elems * 2);
+    const unsigned off = in ? (unsigned)(my_q * q_rs + (16 * kk + 8 * h) * 2) : q_ext;
     qf[kk] = buf_load16(rq, off);
   }
 
@@ -691,7 +709,7 @@ void attn_fwd_kernel(Params p) {
   const float inv = 1.0f / (l_norm + partner(l_norm));
   const float l_exact = LSE ? l_run + partner(l_run) : 0.f;   // (all lanes take part)
   if (my_q < L) {
-    unsigned char* orow = p.o + ((size_t)bh * head_elems + (size_t)my_q * D) * 2;
+    unsigned char* orow = p.o + (size_t)(bi * p.lo.sb + hi * p.lo.sh + (long long)my_q * p.lo.sr) * 2;
 #pragma unroll
     for (int dt = 0; dt < C::DTL; ++dt)
 #pragma unroll
@@ -782,6 +800,22 @@ attn_status_t validate(const Problem& pr) {
   return ATTN_OK;
 }
 
+// One tensor's element strides (batch, head, row; D contiguous): non-negative, rows at least D
+// apart (so row L of a head starts past the head's last element, which the kernel relies on to
+// read rows past L as zeros), one head's rows within 2^31 bytes (32-bit buffer offsets), and every
+// element offset within int64.
+attn_status_t validate_layout(const Problem& pr, const int64_t* st, int64_t elem_bytes) {
+  const int64_t sb = st[0], sh = st[1], sr = st[2];
+  const int64_t lim = (int64_t)1 << 31;
+  if (sb < 0 || sh < 0 || sr < pr.D || sr >= lim) return ATTN_ERR_SHAPE;
+  if (pr.batch == 0 || pr.heads == 0 || pr.L == 0) return ATTN_OK;
+  const __int128 extent = ((__int128)(pr.L - 1) * sr + pr.D) * elem_bytes;
+  if (extent >= lim) return ATTN_ERR_SHAPE;
+  const __int128 last = (__int128)(pr.batch - 1) * sb + (__int128)(pr.heads - 1) * sh + extent / elem_bytes;
+  if (last * elem_bytes > (__int128)INT64_MAX) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
 template <int D, int DT>
 hipError_t dispatch_dense(int mode, const Params& p, hipStream_t s) {
   // 4 waves (128 query rows) per workgroup and 64-key tiles for every head dim: two waves per
@@ -838,14 +872,23 @@ attn_status_t attn_fwd_check(int64_t batch, int64_t heads, int64_t L, int64_t D,
   return validate(pr);
 }
 
-attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int64_t batch, int64_t heads, int64_t L, int64_t D, float sm_scale,
-                           attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype,
-                           void* stream) {
+attn_status_t attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t batch, int64_t heads, int64_t L, int64_t D,
+                               const int64_t* q_strides, const int64_t* k_strides,
+                               const int64_t* v_strides, const int64_t* o_strides, float sm_scale,
+                               attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype,
+                               void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  if (q_strides == nullptr || k_strides == nullptr || v_strides == nullptr || o_strides == nullptr)
+    return ATTN_ERR_NULL;
   Problem pr{batch, heads, L, D, sm_scale, (int)mask_mode, block_size, (int)dtype};
-  const attn_status_t st = validate(pr);
+  attn_status_t st = validate(pr);
   if (st != ATTN_OK) return st;
+  const int64_t vb = (dtype == ATTN_BF16_V_E5M2 || dtype == ATTN_F16_V_E5M2) ? 1 : 2;
+  if ((st = validate_layout(pr, q_strides, 2)) != ATTN_OK) return st;
+  if ((st = validate_layout(pr, k_strides, 2)) != ATTN_OK) return st;
+  if ((st = validate_layout(pr, v_strides, vb)) != ATTN_OK) return st;
+  if ((st = validate_layout(pr, o_strides, 2)) != ATTN_OK) return st;
   if (batch * heads * L == 0) return ATTN_OK;
   Params p{};
   p.q = (const unsigned char*)q;
@@ -853,11 +896,30 @@ attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, void* o,
   p.v = (const unsigned char*)v;
   p.o = (unsigned char*)o;
   p.lse = lse;
+  p.lq = Layout{q_strides[0], q_strides[1], (int)q_strides[2]};
+  p.lk = Layout{k_strides[0], k_strides[1], (int)k_strides[2]};
+  p.lv = Layout{v_strides[0], v_strides[1], (int)v_strides[2]};
+  p.lo = Layout{o_strides[0], o_strides[1], (int)o_strides[2]};
+  p.heads = (int)heads;
   p.L = (int)L;
   p.bh = (int)(batch * heads);
   p.c = sm_scale * kLog2e;
   const hipError_t e = dispatch(pr, p, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t batch, int64_t heads, int64_t L, int64_t D, float sm_scale,
+                           attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype,
+                           void* stream) {
+  // contiguous [batch, heads, L, D]; the stride products are formed only for sizes that pass
+  // validation (which bounds them far below int64)
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULL;
+  const attn_status_t vs = validate(Problem{batch, heads, L, D, sm_scale, (int)mask_mode, block_size, (int)dtype});
+  if (vs != ATTN_OK) return vs;
+  const int64_t st[3] = {heads * L * D, L * D, D};
+  return attn_fwd_strided(q, k, v, o, lse, batch, heads, L, D, st, st, st, st, sm_scale, mask_mode,
+                          block_size, dtype, stream);
 }
 
 attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t batch,

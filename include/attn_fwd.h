@@ -106,6 +106,30 @@ attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, void* o,
                            attn_dtype_t dtype, void* stream);
 
 /*
+ * attn_fwd_strided -- attn_fwd_lse on tensors in any layout whose last dimension (D) is contiguous,
+ * such as [batch, L, heads, D] or a slice of a wider tensor.  The pages' kernels take the element
+ * strides of every dimension as arguments ("TLX Block Attention", kernel arguments; "Triton-CUDA
+ * Attention" and "Fused Attention", stride arguments of the kernels).
+ *
+ *   x_strides    host pointers to three int64 element strides of tensor x: batch, head, row
+ *                (sequence position).  Element (b, h, i, d) of x sits at
+ *                x + (b*x_strides[0] + h*x_strides[1] + i*x_strides[2] + d) elements.
+ *   lse          as in attn_fwd_lse: NULL, or a contiguous fp32 [batch, heads, L] array.
+ *
+ * Requirements (else ATTN_ERR_SHAPE, nothing enqueued): strides non-negative; the row stride at
+ * least D (rows of one head do not overlap); one head's rows of one tensor span fewer than 2^31
+ * bytes; every element offset fits int64.  o must not overlap itself, q, k or v.  A NULL
+ * stride pointer returns ATTN_ERR_NULL.  attn_fwd and attn_fwd_lse are this call with the
+ * contiguous strides (heads*L*D, L*D, D).
+ */
+attn_status_t attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t batch, int64_t heads, int64_t L, int64_t D,
+                               const int64_t* q_strides, const int64_t* k_strides,
+                               const int64_t* v_strides, const int64_t* o_strides, float sm_scale,
+                               attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype,
+                               void* stream);
+
+/*
  * attn_fwd_check -- run attn_fwd's host-side validation only (no HIP call, pointers may be
  * any non-NULL value).  Returns the status attn_fwd would return before launching.
  */

@@ -30,7 +30,7 @@ def _declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == ["attn_abi_version", "attn_fwd", "attn_fwd_check",
-                                     "attn_fwd_lse", "attn_status_str"]
+                                     "attn_fwd_lse", "attn_fwd_strided", "attn_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -137,3 +137,39 @@ def test_python_binding_rejects_cpu_tensors():
         binding.attn_fwd(x, x, x)
     with pytest.raises(ValueError):
         binding.attn_fwd(x, x, x, mask="sliding")
+
+
+def _strided(lib, B=1, H=2, L=64, D=128, q=None, k=None, v=None, o=None, dt=F16, mode=NONE, bs=0,
+             null=None):
+    cont = (H * L * D, L * D, D)
+    arrs = []
+    for name, st in (("q", q), ("k", k), ("v", v), ("o", o)):
+        arrs.append(None if null == name else (ctypes.c_int64 * 3)(*(st if st is not None else cont)))
+    return lib.attn_fwd_strided(FAKE, FAKE, FAKE, FAKE, None, B, H, L, D, *arrs, 0.125, mode, bs,
+                                dt, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_strided_null_stride_pointer(lib, which):
+    assert _strided(lib, null=which) == binding.Status.ERR_NULL
+
+
+@pytest.mark.parametrize("args", [
+    dict(q=(64 * 2 * 128, 128, 100)),            # row stride below D: rows overlap
+    dict(k=(-1, 64 * 128, 128)),                 # negative batch stride
+    dict(v=(0, -128, 128)),                      # negative head stride
+    dict(o=(2 * 64 * 128, 64 * 128, 1 << 31)),   # row stride beyond int32
+    dict(L=1 << 16, D=128, q=(0, 0, 1 << 15)),   # one head's rows span >= 2^31 bytes
+    dict(B=2, H=2, q=((1 << 62), 0, 128)),       # element offsets overflow int64
+])
+def test_strided_layouts_rejected(lib, args):
+    assert _strided(lib, **args) == binding.Status.ERR_SHAPE
+
+
+@pytest.mark.parametrize("args", [
+    dict(B=0, q=(64 * 2 * 128, 128, 2 * 128)),   # [B, L, H, D] strides; empty problem: no launch
+    dict(L=0, k=(0, 0, 128)),                    # broadcast over batch and heads; empty
+    dict(H=0, v=(1000, 7, 4096)),
+])
+def test_strided_layouts_accepted_without_launch(lib, args):
+    assert _strided(lib, **args) == binding.Status.OK

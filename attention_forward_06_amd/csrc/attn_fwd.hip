@@ -28,8 +28,13 @@
 //   * fp8 V: P is rounded to OCP e5m2 (v_cvt_pk_bf8_f32, round-to-nearest-even) and P.V runs
 //     on v_mfma_f32_32x32x64_f8f6f4 with both operands in bf8 (e5m2) format; the row sum uses
 //     the unrounded fp32 P ("Fused Attention", _attn_fwd_inner fp8 branch).
-//   * K/V tiles are staged HBM -> VGPR -> LDS with 128-bit buffer loads (rows past L read as
-//     zero), prefetching tile t+1 while tile t is consumed.
+//   * 16-bit P: the accumulator is rescaled only when a row max outgrows its reference by more
+//     than 2^8, and O is normalised by the sum of the rounded weights P.V used (see Cfg).
+//   * K/V tiles go HBM -> LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane, rows past L
+//     read as zero), double-buffered with one barrier per tile; a software pipeline keeps K one
+//     tile ahead of V so the score MFMAs of tile t+1 overlap the softmax of tile t.
+//   * Any layout with a contiguous head dim (per-tensor batch / head / row strides); head dim 16
+//     runs the head-dim-32 tiles with zero upper halves.
 //   * Workgroup ids are remapped so all query blocks of one (batch, head) land on the same
 //     XCD (its K/V stays in that XCD's L2); causal blocks run longest first within small head
 //     groups, so the CUs of an XCD finish together.
@@ -131,8 +136,6 @@ __device__ __forceinline__ int key_of_row(int rho) {
   return (rho & 0x13) | ((rho & 4) << 1) | ((rho >> 1) & 4);
 }
 
-__device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32); }
 
 template <int D, int DT, int MODE, int NW, int BN, int KW = BN>
 struct Cfg {
@@ -156,7 +159,6 @@ struct Cfg {
   static constexpr int KTILE = BN * KROWB;
   static constexpr int VTILE = BN * VROWB;
   static constexpr int NBUF = MODE == kMaskBlock ? 1 : 2;   // double-buffer the streamed tiles
-  static constexpr int LDS_BYTES = NBUF * (KTILE + VTILE);
   static constexpr int KDMA = KTILE / 1024 / NW;  // 1 KiB LDS-DMA instructions per wave per K tile
   static constexpr int VDMA = VTILE / 1024 / NW;
   // Period (in DMA instruction index i) of a lane's swizzled offset: instruction i starts

@@ -101,6 +101,24 @@ def test_workload_full_size(name):
     assert worst <= TOL[dt]
 
 
+@pytest.mark.parametrize("mode,D,dtype", [("causal", 128, "bf16"), ("none", 64, "f16")])
+def test_long_sequence_sampled_rows(mode, D, dtype):
+    # L = 65536: the longest key loop and the largest in-head offsets among the tests
+    B, H, L = 1, 2, 65536
+    q, k, v = gpu_qkv(B, H, L, D, dtype, seed=21, gen_device="cuda")
+    o = run(q, k, v, mode, 0, default_scale(D))
+    assert torch.isfinite(o.float()).all()
+    rows = sample_rows(L, n_edge=32, n_rand=64)
+    worst = 0.0
+    for h in range(H):
+        qn, kn, vn = (to_f64(x[:, h:h + 1]) for x in (q, k, v))
+        ref = oracle.attn_ref(qn, kn, vn, mode, default_scale(D), rows=rows)
+        got = to_f64(o[:, h:h + 1][:, :, torch.from_numpy(rows).cuda()])
+        worst = max(worst, float(np.abs(got - ref).max()))
+    _report(f"L=65536 {mode} D{D} {dtype} (rows {rows.size} x heads {H})", worst, TOL[dtype])
+    assert worst <= TOL[dtype]
+
+
 def test_block_diag_quick_check_of_the_page():
     # The block-diagonal page checks block 0 of head 0 of (1,2,256,128) fp16, seed 42, bs 64,
     # against full attention on that 64-row slice, expecting fp16-level agreement (~1e-3).

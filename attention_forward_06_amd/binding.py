@@ -139,6 +139,8 @@ def attn_fwd(q, k, v, mask="none", block_size=0, sm_scale=None, out=None, return
             out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     elif out.shape != q.shape or out.dtype != q.dtype or (out.stride(3) != 1 and D > 1):
         raise ValueError("out must be shaped and typed like q with a contiguous last dimension")
+    elif out.device != q.device:
+        raise ValueError("out must be on q's device")
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
     stream = torch.cuda.current_stream(q.device).cuda_stream
     lse_ptr = lse.data_ptr() if lse is not None else None

@@ -182,6 +182,10 @@ struct Cfg {
   // The fp8 path keeps the pages' sum over the unrounded p (P is far coarser there).
   static constexpr bool HAT = !V8;
   static constexpr int WAVES_PER_EU = (D >= 256) ? 1 : 2;
+  // With two waves on a SIMD, the one in its MFMA stretch (S(t+1), the exponentials of P(t),
+  // P(t).V(t)) is raised above the other, which is then in its barrier / DMA / row-max stretch:
+  // the matrix core gets the shared issue port first.  With one wave per SIMD there is no rival.
+  static constexpr bool PRIO = WAVES_PER_EU > 1;
   static_assert(BN % 32 == 0, "key tile is a whole number of 32-key subtiles");
   static_assert(!V8 || BN % 64 == 0, "fp8 P.V consumes 64 keys per MFMA");
   static_assert(KTILE % (1024 * NW) == 0 && VTILE % (1024 * NW) == 0,
@@ -617,10 +621,12 @@ void attn_fwd_kernel(Params p) {
     bool live[C::KT], masked[C::KT];
     tile_flags(t, fast || t < nfull, live, masked);
     softmax_max(t, s_cur, live, masked);       // VALU: mask, row max, rescale
+    if constexpr (C::PRIO) __builtin_amdgcn_s_setprio(1);
     if (has_next) scores(s_nxt, fr, kb_nxt, live_n, ksw);   // MFMA: S(t+1) ...
     u32x4 pk[KW / 16];
     softmax_exp(s_cur, pk, live);              // ... while the VALU exponentiates P(t)
     pv(s_cur, pk, vb_cur, live);               // MFMA: O += P(t) V(t)
+    if constexpr (C::PRIO) __builtin_amdgcn_s_setprio(0);
     if constexpr (D <= 128 && C::KT == 2 && !C::V8 && MODE != kMaskBlock) {
       if (fast && has_next) {
         // Issue order of the unmasked iteration: each score MFMA of subtile 0 followed by one K

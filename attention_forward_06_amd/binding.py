@@ -24,6 +24,7 @@ class Status:
 
 
 _lib = None
+_ceilings = None
 
 
 def library_path():
@@ -155,3 +156,40 @@ def attn_fwd(q, k, v, mask="none", block_size=0, sm_scale=None, out=None, return
     if st != Status.OK:
         raise RuntimeError(f"attn_fwd failed: {status_str(st)} (status {st})")
     return (out, lse) if return_lse else out
+
+
+def load_ceilings():
+    """Load libattn_ceilings.so (once): the roofline's calibration kernels, not attention."""
+    global _ceilings
+    if _ceilings is not None:
+        return _ceilings
+    path = os.path.join(HERE, "libattn_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run attention_forward_06_amd.build.build() first")
+    lib = ctypes.CDLL(path)
+    lib.attn_ceiling_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.attn_ceiling_mfma_bf16.restype = ctypes.c_int
+    lib.attn_ceiling_hbm_3r1w.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_size_t,
+                                          ctypes.POINTER(ctypes.c_double)]
+    lib.attn_ceiling_hbm_3r1w.restype = ctypes.c_int
+    _ceilings = lib
+    return lib
+
+
+def ceiling_mfma_bf16(warmup, launches):
+    """Sustained dense bf16 MFMA rate (TFLOP/s) with random operands; synchronises the device."""
+    out = ctypes.c_double()
+    st = load_ceilings().attn_ceiling_mfma_bf16(int(warmup), int(launches), ctypes.byref(out))
+    if st != 0:
+        raise RuntimeError(f"attn_ceiling_mfma_bf16 failed: hipError {st}")
+    return out.value
+
+
+def ceiling_hbm_3r1w(warmup, launches, bytes_per_array):
+    """Sustained HBM rate (GB/s) reading three arrays and writing one; synchronises the device."""
+    out = ctypes.c_double()
+    st = load_ceilings().attn_ceiling_hbm_3r1w(int(warmup), int(launches), int(bytes_per_array),
+                                                ctypes.byref(out))
+    if st != 0:
+        raise RuntimeError(f"attn_ceiling_hbm_3r1w failed: hipError {st}")
+    return out.value

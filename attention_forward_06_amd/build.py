@@ -1,7 +1,8 @@
-"""Build libattn_fwd.so (gfx950) in-tree with hipcc.
+"""Build libattn_fwd.so and libattn_ceilings.so (gfx950) in-tree with hipcc.
 
-Always recompiles.  The library is written next to this file so that it travels
-with the source tree; nothing is installed elsewhere.
+Always recompiles.  The libraries are written next to this file so that they travel
+with the source tree; nothing is installed elsewhere.  libattn_ceilings.so holds the
+calibration kernels of the roofline (measured MFMA and HBM ceilings), not attention.
 """
 import os
 import subprocess
@@ -12,6 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip")]
 LIBRARY = os.path.join(HERE, "libattn_fwd.so")
+CEILINGS_SOURCES = [os.path.join(HERE, "csrc", "ceilings.hip")]
+CEILINGS_LIBRARY = os.path.join(HERE, "libattn_ceilings.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -35,28 +38,43 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose=False, resource_report=None):
-    """Compile the HIP sources into LIBRARY; returns its path.
-
-    resource_report: optional path; when given, the compiler's per-kernel register /
-    LDS / occupancy remarks are written there.
-    """
-    fd, tmp = tempfile.mkstemp(prefix=".libattn_fwd.", suffix=".so.tmp", dir=HERE)
+def _start(sources, library, verbose, resource_report=None):
+    """Launch hipcc for one library into a temporary file; returns (process, tmp, library)."""
+    stem = os.path.splitext(os.path.basename(library))[0]
+    fd, tmp = tempfile.mkstemp(prefix=f".{stem}.", suffix=".so.tmp", dir=HERE)
     os.close(fd)
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + SOURCES
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + sources
     if resource_report:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if resource_report:
-        with open(resource_report, "w") as f:
-            f.write(res.stdout + res.stderr)
-    if res.returncode != 0:
-        os.unlink(tmp)
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    os.replace(tmp, LIBRARY)
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    return proc, tmp, library
+
+
+def build(verbose=False, resource_report=None):
+    """Compile the HIP sources into LIBRARY and CEILINGS_LIBRARY; returns LIBRARY's path.
+
+    resource_report: optional path; when given, the compiler's per-kernel register /
+    LDS / occupancy remarks for LIBRARY are written there.
+    """
+    jobs = [_start(SOURCES, LIBRARY, verbose, resource_report),
+            _start(CEILINGS_SOURCES, CEILINGS_LIBRARY, verbose)]
+    failed = []
+    for i, (proc, tmp, library) in enumerate(jobs):
+        out, err = proc.communicate()
+        if i == 0 and resource_report:
+            with open(resource_report, "w") as f:
+                f.write(out + err)
+        if proc.returncode != 0:
+            os.unlink(tmp)
+            sys.stderr.write(out + err)
+            failed.append((library, proc.returncode))
+        else:
+            os.replace(tmp, library)
+    if failed:
+        raise RuntimeError("hipcc failed: " + ", ".join(f"{os.path.basename(l)} (status {c})"
+                                                        for l, c in failed))
     return LIBRARY
 
 

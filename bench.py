@@ -47,6 +47,8 @@ def parse():
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured MFMA / HBM ceilings (e.g. under a counter profiler)")
     return ap.parse_args()
 
 
@@ -137,6 +139,20 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     del x, y
+
+
+def measured_ceilings():
+    """What the chip sustains on the two bounding resources, measured after the timed workloads
+    (so they cannot disturb them): back-to-back bf16 MFMAs with random operands, and HBM streaming
+    in the block-diagonal mix (three arrays read, one written)."""
+    from attention_forward_06_amd import binding
+    mfma = binding.ceiling_mfma_bf16(warmup=2000, launches=4000)
+    hbm = binding.ceiling_hbm_3r1w(warmup=5, launches=40, bytes_per_array=512 << 20)
+    return {"mfma_bf16_TFLOP_per_s": round(mfma, 1), "hbm_3read_1write_GB_per_s": round(hbm, 1),
+            "how": "mfma: v_mfma_f32_32x32x16_bf16 back to back, 2 waves per SIMD on every CU, "
+                   "random operands changing every MFMA, 4000 launches after 2000 warm-up; hbm: "
+                   "d = a ^ b ^ c over 512 MiB arrays, 16-byte non-temporal accesses, 40 launches "
+                   "after 5 warm-up"}
 
 
 def cpu_baseline(target_s):
@@ -241,6 +257,12 @@ def main():
     if others:
         line["other_workloads"] = others
     line["launch_spread_ms"] = {"min": round(head["min_ms"], 5), "median": round(head["median_ms"], 5)}
+    if not a.no_ceilings:
+        ceil = measured_ceilings()
+        ceil["headline_frac"] = round(head["tflops"] / ceil["mfma_bf16_TFLOP_per_s"], 4)
+        for key, b in bd.items():
+            ceil[f"block_diag_{key}_frac"] = round(b["GB_per_s"] / ceil["hbm_3read_1write_GB_per_s"], 4)
+        line["measured_ceilings"] = ceil
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -143,16 +143,18 @@ def attn_fwd(q, k, v, mask="none", block_size=0, sm_scale=None, out=None, return
     elif out.device != q.device:
         raise ValueError("out must be on q's device")
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
-    stream = torch.cuda.current_stream(q.device).cuda_stream
     lse_ptr = lse.data_ptr() if lse is not None else None
-    if all(t.is_contiguous() for t in (q, k, v, out)):
-        st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, D,
-                          float(sm_scale), mask, block_size, dtype, stream, lse_ptr)
-    else:
-        strides = [t.stride()[:3] for t in (q, k, v, out)]
-        st = attn_fwd_strided_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H,
-                                  L, D, strides, float(sm_scale), mask, block_size, dtype, stream,
-                                  lse_ptr)
+    # the library launches on the current HIP device: make it the tensors' device
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        if all(t.is_contiguous() for t in (q, k, v, out)):
+            st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, D,
+                              float(sm_scale), mask, block_size, dtype, stream, lse_ptr)
+        else:
+            strides = [t.stride()[:3] for t in (q, k, v, out)]
+            st = attn_fwd_strided_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B,
+                                      H, L, D, strides, float(sm_scale), mask, block_size, dtype,
+                                      stream, lse_ptr)
     if st != Status.OK:
         raise RuntimeError(f"attn_fwd failed: {status_str(st)} (status {st})")
     return (out, lse) if return_lse else out

@@ -16,7 +16,7 @@ import torch
 
 DTYPES = ("f16", "bf16", "bf16_v_e5m2", "f16_v_e5m2")
 
-# The five workloads of the target, named by what they are.
+# Workloads shaped like the pages' (sizes, mask and dtype in the name).
 WORKLOADS = {
     "blockdiag_b1_h2_n256_d128_bs64_f16":
         dict(mode="block_diag", B=1, H=2, L=256, D=128, dtype="f16", block_size=64),

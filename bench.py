@@ -189,8 +189,10 @@ def cpu_baseline(target_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported by this build "
-              "(the attention forward is measured on one MI355X)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported (the "
+              "attention forward is measured on one MI355X; the work is independent per "
+              "(batch, head), so G GPUs would each run the same kernel on their slice)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

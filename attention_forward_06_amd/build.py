@@ -15,6 +15,9 @@ SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip")]
 LIBRARY = os.path.join(HERE, "libattn_fwd.so")
 CEILINGS_SOURCES = [os.path.join(HERE, "csrc", "ceilings.hip")]
 CEILINGS_LIBRARY = os.path.join(HERE, "libattn_ceilings.so")
+# C++ host program that checks the C ABI without Python (links libattn_fwd.so)
+C_CHECK_SOURCE = os.path.join(HERE, "csrc", "c_abi_check.cpp")
+C_CHECK_BINARY = os.path.join(HERE, "c_abi_check")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -75,7 +78,25 @@ def build(verbose=False, resource_report=None):
     if failed:
         raise RuntimeError("hipcc failed: " + ", ".join(f"{os.path.basename(l)} (status {c})"
                                                         for l, c in failed))
+    _build_c_check(verbose)
     return LIBRARY
+
+
+def _build_c_check(verbose):
+    """Compile C_CHECK_SOURCE against the freshly built LIBRARY (rpath: its own directory)."""
+    fd, tmp = tempfile.mkstemp(prefix=".c_abi_check.", suffix=".tmp", dir=HERE)
+    os.close(fd)
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"),
+           C_CHECK_SOURCE, "-L", HERE, "-lattn_fwd", "-Wl,-rpath,$ORIGIN", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        os.unlink(tmp)
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed for {os.path.basename(C_CHECK_BINARY)} "
+                           f"(status {res.returncode})")
+    os.replace(tmp, C_CHECK_BINARY)
 
 
 if __name__ == "__main__":

@@ -112,7 +112,8 @@ def attn_fwd(q, k, v, mask="none", block_size=0, sm_scale=None, out=None, return
     """Attention forward on [batch, heads, L, D] CUDA(HIP) tensors; returns o (and lse).
 
     The tensors may be any views whose last dimension is contiguous (for example a
-    [batch, L, heads, D] tensor permuted to [batch, heads, L, D]); o then takes q's layout.
+    [batch, L, heads, D] tensor permuted to [batch, heads, L, D]) with every stride, in bytes,
+    a multiple of 16 and the data on a 16-byte boundary; o then takes q's layout.
     o has q's dtype; lse is fp32 [batch, heads, L] (natural log of the row normaliser).
     Enqueued on torch's current stream.
     """

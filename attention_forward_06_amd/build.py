@@ -11,7 +11,7 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip"), os.path.join(HERE, "csrc", "attn_api.cpp")]
 LIBRARY = os.path.join(HERE, "libattn_fwd.so")
 CEILINGS_SOURCES = [os.path.join(HERE, "csrc", "ceilings.hip")]
 CEILINGS_LIBRARY = os.path.join(HERE, "libattn_ceilings.so")

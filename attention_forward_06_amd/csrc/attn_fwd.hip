@@ -44,7 +44,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/attn_fwd.h"
+#include "attn_host.h"
 
 namespace {
 
@@ -63,11 +63,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
 
-// Element strides of one [batch, heads, L, D] tensor; D is contiguous.
-struct Layout {
-  long long sb, sh;  // batch, head
-  int sr;            // row (sequence position), >= D
-};
+using attn::Layout;
 
 struct Params {
   const unsigned char* q;
@@ -744,7 +740,7 @@ void attn_fwd_kernel(Params p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Host side: validation, instance table, launch.
+// Host side: instance table and launch (argument checks: attn_api.cpp).
 // ------------------------------------------------------------------------------------------
 
 template <int D, int DT, int MODE, int NW, int BN, int KW = BN>
@@ -773,67 +769,6 @@ hipError_t launch(const Params& p0, hipStream_t stream) {
   return hipGetLastError();
 }
 
-struct Problem {
-  int64_t batch, heads, L, D;
-  float sm_scale;
-  int mode;
-  int64_t block_size;
-  int dtype;
-};
-
-bool supported(const Problem& pr) {
-  const bool dense = pr.mode == kMaskNone || pr.mode == kMaskCausal;
-  if (dense) {
-    if (pr.D == 16 || pr.D == 32 || pr.D == 64 || pr.D == 128) return pr.dtype == kF16 || pr.dtype == kBF16;
-    if (pr.D == 256) return true;
-    return false;
-  }
-  if (pr.D != 64 && pr.D != 128) return false;
-  if (pr.dtype != kF16 && pr.dtype != kBF16) return false;
-  return pr.block_size == 32 || pr.block_size == 64 || pr.block_size == 128;
-}
-
-attn_status_t validate(const Problem& pr) {
-  if (pr.mode < 0 || pr.mode > 2 || pr.dtype < 0 || pr.dtype > 3) return ATTN_ERR_ARG;
-  // finite and positive, checked on the bits (independent of floating-point flags)
-  const uint32_t sbits = __builtin_bit_cast(uint32_t, pr.sm_scale);
-  const bool not_finite = ((sbits >> 23) & 0xffu) == 0xffu;
-  if (not_finite || (sbits >> 31) != 0u || (sbits & 0x7fffffffu) == 0u) return ATTN_ERR_ARG;
-  if (pr.batch < 0 || pr.heads < 0 || pr.L < 0 || pr.D <= 0) return ATTN_ERR_SHAPE;
-  if (pr.mode == kMaskBlock) {
-    if (pr.block_size <= 0) return ATTN_ERR_SHAPE;
-    if (pr.L % pr.block_size != 0) return ATTN_ERR_SHAPE;
-  }
-  // Sizes: every count must fit the kernel's index types.
-  const int64_t lim = (int64_t)1 << 31;
-  if (pr.L >= lim || pr.batch >= lim || pr.heads >= lim) return ATTN_ERR_SHAPE;
-  if (pr.batch > 0 && pr.heads > (INT64_MAX / pr.batch)) return ATTN_ERR_SHAPE;
-  const int64_t bh = pr.batch * pr.heads;
-  if (bh >= lim) return ATTN_ERR_SHAPE;
-  if (pr.L > 0 && pr.D > INT64_MAX / 2 / pr.L) return ATTN_ERR_SHAPE;
-  if (pr.L * pr.D * 2 >= lim) return ATTN_ERR_SHAPE;            // one head must fit 2^31 bytes
-  if (bh > 0 && pr.L * pr.D > INT64_MAX / 2 / bh) return ATTN_ERR_SHAPE;
-  if (((pr.L + 31) / 32) * bh >= lim) return ATTN_ERR_SHAPE;    // workgroup count fits the grid
-  if (!supported(pr)) return ATTN_ERR_UNSUPPORTED;
-  return ATTN_OK;
-}
-
-// One tensor's element strides (batch, head, row; D contiguous): non-negative, rows at least D
-// apart (so row L of a head starts past the head's last element, which the kernel relies on to
-// read rows past L as zeros), one head's rows within 2^31 bytes (32-bit buffer offsets), and every
-// element offset within int64.
-attn_status_t validate_layout(const Problem& pr, const int64_t* st, int64_t elem_bytes) {
-  const int64_t sb = st[0], sh = st[1], sr = st[2];
-  const int64_t lim = (int64_t)1 << 31;
-  if (sb < 0 || sh < 0 || sr < pr.D || sr >= lim) return ATTN_ERR_SHAPE;
-  if (pr.batch == 0 || pr.heads == 0 || pr.L == 0) return ATTN_OK;
-  const __int128 extent = ((__int128)(pr.L - 1) * sr + pr.D) * elem_bytes;
-  if (extent >= lim) return ATTN_ERR_SHAPE;
-  const __int128 last = (__int128)(pr.batch - 1) * sb + (__int128)(pr.heads - 1) * sh + extent / elem_bytes;
-  if (last * elem_bytes > (__int128)INT64_MAX) return ATTN_ERR_SHAPE;
-  return ATTN_OK;
-}
-
 template <int D, int DT>
 hipError_t dispatch_dense(int mode, const Params& p, hipStream_t s) {
   // 4 waves (128 query rows) per workgroup and 64-key tiles for every head dim: two waves per
@@ -852,7 +787,7 @@ hipError_t dispatch_block(int64_t bs, const Params& p, hipStream_t s) {
   return launch<D, DT, kMaskBlock, 4, 128, 128>(p, s);
 }
 
-hipError_t dispatch(const Problem& pr, const Params& p, hipStream_t s) {
+hipError_t dispatch(const attn::Problem& pr, const Params& p, hipStream_t s) {
   if (pr.mode == kMaskBlock) {
     if (pr.D == 64) return pr.dtype == kF16 ? dispatch_block<64, kF16>(pr.block_size, p, s)
                                             : dispatch_block<64, kBF16>(pr.block_size, p, s);
@@ -882,83 +817,24 @@ hipError_t dispatch(const Problem& pr, const Params& p, hipStream_t s) {
 
 }  // namespace
 
-extern "C" {
+namespace attn {
 
-attn_status_t attn_fwd_check(int64_t batch, int64_t heads, int64_t L, int64_t D, float sm_scale,
-                             attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype) {
-  Problem pr{batch, heads, L, D, sm_scale, (int)mask_mode, block_size, (int)dtype};
-  return validate(pr);
-}
-
-attn_status_t attn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int64_t batch, int64_t heads, int64_t L, int64_t D,
-                               const int64_t* q_strides, const int64_t* k_strides,
-                               const int64_t* v_strides, const int64_t* o_strides, float sm_scale,
-                               attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype,
-                               void* stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULL;
-  if (q_strides == nullptr || k_strides == nullptr || v_strides == nullptr || o_strides == nullptr)
-    return ATTN_ERR_NULL;
-  Problem pr{batch, heads, L, D, sm_scale, (int)mask_mode, block_size, (int)dtype};
-  attn_status_t st = validate(pr);
-  if (st != ATTN_OK) return st;
-  const int64_t vb = (dtype == ATTN_BF16_V_E5M2 || dtype == ATTN_F16_V_E5M2) ? 1 : 2;
-  if ((st = validate_layout(pr, q_strides, 2)) != ATTN_OK) return st;
-  if ((st = validate_layout(pr, k_strides, 2)) != ATTN_OK) return st;
-  if ((st = validate_layout(pr, v_strides, vb)) != ATTN_OK) return st;
-  if ((st = validate_layout(pr, o_strides, 2)) != ATTN_OK) return st;
-  if (batch * heads * L == 0) return ATTN_OK;
+int launch(const Problem& pr, const LaunchArgs& a, void* stream) {
   Params p{};
-  p.q = (const unsigned char*)q;
-  p.k = (const unsigned char*)k;
-  p.v = (const unsigned char*)v;
-  p.o = (unsigned char*)o;
-  p.lse = lse;
-  p.lq = Layout{q_strides[0], q_strides[1], (int)q_strides[2]};
-  p.lk = Layout{k_strides[0], k_strides[1], (int)k_strides[2]};
-  p.lv = Layout{v_strides[0], v_strides[1], (int)v_strides[2]};
-  p.lo = Layout{o_strides[0], o_strides[1], (int)o_strides[2]};
-  p.heads = (int)heads;
-  p.L = (int)L;
-  p.bh = (int)(batch * heads);
-  p.c = sm_scale * kLog2e;
-  const hipError_t e = dispatch(pr, p, (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  p.q = (const unsigned char*)a.q;
+  p.k = (const unsigned char*)a.k;
+  p.v = (const unsigned char*)a.v;
+  p.o = (unsigned char*)a.o;
+  p.lse = a.lse;
+  p.lq = a.lq;
+  p.lk = a.lk;
+  p.lv = a.lv;
+  p.lo = a.lo;
+  p.heads = a.heads;
+  p.L = a.L;
+  p.bh = a.bh;
+  p.c = a.c;
+  return (int)dispatch(pr, p, (hipStream_t)stream);
 }
 
-attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int64_t batch, int64_t heads, int64_t L, int64_t D, float sm_scale,
-                           attn_mask_t mask_mode, int64_t block_size, attn_dtype_t dtype,
-                           void* stream) {
-  // contiguous [batch, heads, L, D]; the stride products are formed only for sizes that pass
-  // validation (which bounds them far below int64)
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr) return ATTN_ERR_NULL;
-  const attn_status_t vs = validate(Problem{batch, heads, L, D, sm_scale, (int)mask_mode, block_size, (int)dtype});
-  if (vs != ATTN_OK) return vs;
-  const int64_t st[3] = {heads * L * D, L * D, D};
-  return attn_fwd_strided(q, k, v, o, lse, batch, heads, L, D, st, st, st, st, sm_scale, mask_mode,
-                          block_size, dtype, stream);
-}
-
-attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t batch,
-                       int64_t heads, int64_t L, int64_t D, float sm_scale, attn_mask_t mask_mode,
-                       int64_t block_size, attn_dtype_t dtype, void* stream) {
-  return attn_fwd_lse(q, k, v, o, nullptr, batch, heads, L, D, sm_scale, mask_mode, block_size,
-                      dtype, stream);
-}
-
-const char* attn_status_str(attn_status_t s) {
-  switch (s) {
-    case ATTN_OK: return "ok";
-    case ATTN_ERR_NULL: return "null pointer argument";
-    case ATTN_ERR_SHAPE: return "invalid shape (negative size, overflow, or block_size not dividing L)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported (mask mode, head dim, dtype, block size) combination";
-    case ATTN_ERR_HIP: return "HIP runtime error at launch";
-    case ATTN_ERR_ARG: return "invalid scalar argument (enum value or sm_scale)";
-  }
-  return "unknown status";
-}
-
-int attn_abi_version(void) { return ATTN_ABI_VERSION; }
-
-}  // extern "C"
+}  // namespace attn

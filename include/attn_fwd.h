@@ -23,8 +23,9 @@
  *                         softmax ("TLX Block Attention", problem statement and kernel).
  *
  * Memory: q, k, v, o are device pointers owned by the caller, each a contiguous
- * [batch, heads, L, D] array (D fastest), the layout every page uses.  o has Q's
- * element type and must not overlap q, k or v.  The library allocates nothing,
+ * [batch, heads, L, D] array (D fastest), the layout every page uses, starting on a
+ * 16-byte boundary (as every HIP allocation does).  o has Q's element type and must not
+ * overlap q, k or v.  The library allocates nothing,
  * frees nothing and never synchronises: the work is enqueued on `stream` (a
  * hipStream_t; NULL is the default stream) and the call returns.
  *
@@ -63,7 +64,8 @@ typedef enum {
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,         /* a required pointer is NULL                                   */
-    ATTN_ERR_SHAPE = 2,        /* negative size, size overflow, or block_size not dividing L    */
+    ATTN_ERR_SHAPE = 2,        /* negative size, size overflow, block_size not dividing L, or a
+                                  pointer or stride off its required boundary                   */
     ATTN_ERR_UNSUPPORTED = 3,  /* (mode, D, dtype, block_size) outside the supported set        */
     ATTN_ERR_HIP = 4,          /* the HIP runtime reported an error at launch                   */
     ATTN_ERR_ARG = 5           /* bad scalar: unknown enum value, sm_scale not finite or <= 0  */
@@ -117,8 +119,9 @@ attn_status_t attn_fwd_lse(const void* q, const void* k, const void* v, void* o,
  *   lse          as in attn_fwd_lse: NULL, or a contiguous fp32 [batch, heads, L] array.
  *
  * Requirements (else ATTN_ERR_SHAPE, nothing enqueued): strides non-negative; the row stride at
- * least D (rows of one head do not overlap); one head's rows of one tensor span fewer than 2^31
- * bytes; every element offset fits int64.  o must not overlap itself, q, k or v.  A NULL
+ * least D (rows of one head do not overlap); every stride, in bytes, a multiple of 16 and q, k,
+ * v, o on 16-byte boundaries (lse on 4: the kernels move rows in 16-byte pieces); one head's
+ * rows of one tensor span fewer than 2^31 bytes; every element offset fits int64.  o must not overlap itself, q, k or v.  A NULL
  * stride pointer returns ATTN_ERR_NULL.  attn_fwd and attn_fwd_lse are this call with the
  * contiguous strides (heads*L*D, L*D, D).
  */

@@ -169,7 +169,35 @@ def test_strided_layouts_rejected(lib, args):
 @pytest.mark.parametrize("args", [
     dict(B=0, q=(64 * 2 * 128, 128, 2 * 128)),   # [B, L, H, D] strides; empty problem: no launch
     dict(L=0, k=(0, 0, 128)),                    # broadcast over batch and heads; empty
-    dict(H=0, v=(1000, 7, 4096)),
+    dict(H=0, v=(1000 * 8, 8, 4096)),            # strides on 16-byte boundaries; empty
 ])
 def test_strided_layouts_accepted_without_launch(lib, args):
     assert _strided(lib, **args) == binding.Status.OK
+
+
+@pytest.mark.parametrize("args", [
+    dict(H=0, v=(1000, 7, 4096)),                # head stride of 14 bytes
+    dict(B=0, q=(64 * 2 * 128 + 4, 128, 2 * 128)),  # batch stride of 8 bytes past a boundary
+    dict(L=0, o=(0, 0, 132)),                    # rows of 264 bytes
+    dict(dt=V8, D=256, v=(0, 0, 264)),           # fp8 V rows of 264 bytes (1 byte per element)
+])
+def test_strided_layouts_off_16_byte_boundaries_rejected(lib, args):
+    assert _strided(lib, **args) == binding.Status.ERR_SHAPE
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+@pytest.mark.parametrize("offset", [2, 8])
+def test_misaligned_base_pointers_rejected(lib, which, offset):
+    kw = {which: FAKE + offset}
+    assert _call(lib, **kw) == binding.Status.ERR_SHAPE
+    ptrs = {n: FAKE for n in "qkvo"}
+    ptrs[which] = FAKE + offset
+    cont = (ctypes.c_int64 * 3)(64 * 128, 64 * 128, 128)
+    st = lib.attn_fwd_strided(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], None, 1, 1, 64, 128,
+                              cont, cont, cont, cont, 0.125, NONE, 0, F16, None)
+    assert st == binding.Status.ERR_SHAPE
+
+
+def test_misaligned_lse_pointer_rejected(lib):
+    assert lib.attn_fwd_lse(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 1, 1, 64, 128, 0.125, NONE, 0, F16,
+                            None) == binding.Status.ERR_SHAPE

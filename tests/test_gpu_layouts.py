@@ -132,22 +132,26 @@ def test_random_problem_sweep(mode, D, dtype, bs, L, B, H, layout, seed):
     out = binding.attn_fwd(q, k, v, mask=mode, block_size=bs)
     torch.cuda.synchronize()
     qn, kn, vn, on = to_f64(q), to_f64(k), to_f64(v), to_f64(out)
+    plain_bar = None
     if dtype in V8_DTYPES:
-        # fp8 P: gate on the pages' recurrence (P rounded against the running max of 64-key
-        # tiles), which the kernel follows; its gap to the plain definition with the cast is a
-        # statistical effect of the rounding frames and reaches ~5e-2 on some inputs.  Against
-        # the recurrence the bar is 2e-2: the kernel evaluates each weight in fp32, the oracle in
-        # fp64, so a weight at an e5m2 rounding midpoint can round the other way, and one e5m2
-        # ulp is a quarter of the weight (one such flip moved O by ~1e-2 in this sweep).
-        plain = float(np.abs(on - oracle.attn_ref(qn, kn, vn, mode, default_scale(D), bs,
-                                                  p_round="e5m2")).max())
+        # fp8 P: the kernel follows the pages' recurrence (P rounded against the running max of
+        # 64-key tiles).  Against that recurrence in fp64 the bar is 2e-2: the kernel evaluates
+        # each weight in fp32, the oracle in fp64, so a weight at an e5m2 rounding midpoint can
+        # round the other way, and one e5m2 ulp is a quarter of the weight.  Against the plain
+        # definition with the cast (final-max frame) the bar is 5e-2, widened only where the
+        # pages' own recurrence is itself farther than that from the definition.
+        r1 = oracle.attn_ref(qn, kn, vn, mode, default_scale(D), bs, p_round="e5m2")
         ref = oracle.attn_online_ref(qn, kn, vn, mode, default_scale(D), 64, bs, p_round="e5m2")
+        plain = float(np.abs(on - r1).max())
+        plain_bar = max(5e-2, float(np.abs(ref - r1).max()) + 2e-2)
         tol = 2e-2
     else:
         plain = None
         ref = oracle.attn_ref(qn, kn, vn, mode, default_scale(D), bs)
         tol = TOL[dtype]
     err = float(np.abs(on - ref).max())
-    extra = f" (plain definition {plain:.3e})" if plain is not None else ""
+    extra = f" (plain definition {plain:.3e}, bar {plain_bar:.3e})" if plain is not None else ""
     print(f"[sweep] {mode} D{D} {dtype} bs{bs} L{L} B{B} H{H} {layout}: {err:.3e}{extra}", flush=True)
     assert err <= tol
+    if plain is not None:
+        assert plain <= plain_bar

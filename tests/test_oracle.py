@@ -208,15 +208,55 @@ def test_online_single_tile_rounding_matches_final_frame():
     assert np.abs(a - c).max() > 1e-3
 
 
-def test_online_rounding_uses_running_max_frame():
-    # Hand-built row: key 0 has score 0, key 1 has score ln(8).  Tile width 1.
-    # Tile 0: m=0, p=1 (exact in e5m2).  Tile 1: m=ln8, alpha=1/8, p=1.
-    # acc = 1*v0/8 + 1*v1; l = 1/8 + 1 -> o = (v0/8 + v1)/(9/8) = (v0 + 8 v1)/9 exactly.
+def _frame_case():
+    """One query row, two keys with scores 0 and ln 2.6 (sm_scale 1), v = (7, 14).
+
+    Worked by hand from the fused-attention page's fp8 branch (_attn_fwd_inner: p is taken
+    against the running max, cast to e5m2 for P.V, the row sum uses the uncast p):
+      tile width 1, running frame: tile 0 has m = 0, p = 1 (exact in e5m2), acc = 7, l = 1;
+        tile 1 has m = ln 2.6, alpha = 1/2.6, p = 1, so acc = 7/2.6 + 14, l = 1/2.6 + 1 and
+        o = (7 + 14 * 2.6) / 3.6 = 217/18 = 12.0555...
+      one tile (width 2), i.e. the final-max frame of the plain definition with the cast:
+        weights 1/2.6 -> e5m2 0.375 (the grid in [0.25, 0.5) is 0.25, 0.3125, 0.375, 0.4375)
+        and 1; o = (0.375 * 7 + 14) / (1/2.6 + 1) = 1729/144 = 12.00694...
+      rounding in the previous frame instead (tile 1's weight taken against m = 0 is 2.6 ->
+        e5m2 2.5, then rescaled by 1/2.6): o = (7 + 2.5 * 14) / 3.6 = 35/3 = 11.666...
+    The three frames give three different answers, so the rounding frame is pinned.
+    """
     q = np.array([[[[1.0], [1.0]]]])
-    k = np.array([[[[0.0], [math.log(8.0)]]]])
-    v = np.array([[[[9.0], [18.0]]]])
+    k = np.array([[[[0.0], [math.log(2.6)]]]])
+    v = np.array([[[[7.0], [14.0]]]])
+    return q, k, v
+
+
+RUNNING_FRAME_O = 217.0 / 18.0
+FINAL_FRAME_O = 1729.0 / 144.0
+
+
+def test_online_rounding_uses_running_max_frame():
+    q, k, v = _frame_case()
     o = oracle.attn_online_ref(q, k, v, "none", 1.0, 1, p_round="e5m2")
-    assert abs(o[0, 0, 1, 0] - (9.0 + 8 * 18.0) / 9.0) <= 1e-12
+    assert abs(o[0, 0, 1, 0] - RUNNING_FRAME_O) <= 1e-12
+    # one tile: the running max is the final max
+    o1 = oracle.attn_online_ref(q, k, v, "none", 1.0, 2, p_round="e5m2")
+    assert abs(o1[0, 0, 1, 0] - FINAL_FRAME_O) <= 1e-12
+    # row 0 sees its own key only in causal mode: weight 1, exact
+    oc = oracle.attn_online_ref(q, k, v, "causal", 1.0, 1, p_round="e5m2")
+    assert oc[0, 0, 0, 0] == 7.0 and abs(oc[0, 0, 1, 0] - RUNNING_FRAME_O) <= 1e-12
+
+
+def test_plain_definition_rounds_in_final_frame():
+    # R1: the plain definition with the cast rounds exp(S - m_final), divides by the uncast sum
+    q, k, v = _frame_case()
+    o = oracle.attn_ref(q, k, v, "none", 1.0, p_round="e5m2")
+    assert abs(o[0, 0, 1, 0] - FINAL_FRAME_O) <= 1e-12
+    # an earlier hand-built row whose weights (1 and 1/8) are exact in e5m2: every frame agrees
+    q8 = np.array([[[[1.0], [1.0]]]])
+    k8 = np.array([[[[0.0], [math.log(8.0)]]]])
+    v8 = np.array([[[[9.0], [18.0]]]])
+    for fn in (lambda: oracle.attn_online_ref(q8, k8, v8, "none", 1.0, 1, p_round="e5m2"),
+               lambda: oracle.attn_ref(q8, k8, v8, "none", 1.0, p_round="e5m2")):
+        assert abs(fn()[0, 0, 1, 0] - (9.0 + 8 * 18.0) / 9.0) <= 1e-12
 
 
 # ---------------------------------------------------------------- row normaliser (LSE)
@@ -301,6 +341,17 @@ def _pin_suite(mod):
                 return False
     if not np.array_equal(mod.attn_ref(q, k, v, "causal", 0.45)[:, :, 0], v[:, :, 0]):
         return False
+    # rounded P: the running-max frame of the recurrence and the final frame of the definition
+    fq, fk, fv = _frame_case()
+    if abs(mod.attn_online_ref(fq, fk, fv, "none", 1.0, 1, p_round="e5m2")[0, 0, 1, 0]
+           - RUNNING_FRAME_O) > 1e-12:
+        return False
+    if abs(mod.attn_ref(fq, fk, fv, "none", 1.0, p_round="e5m2")[0, 0, 1, 0] - FINAL_FRAME_O) > 1e-12:
+        return False
+    # one tile of width 2: the weight 1/2.6 is cast to 0.375 for P.V, the sum keeps 1/2.6
+    if abs(mod.attn_online_ref(fq, fk, fv, "none", 1.0, 2, p_round="e5m2")[0, 0, 1, 0]
+           - FINAL_FRAME_O) > 1e-12:
+        return False
     return True
 
 
@@ -318,6 +369,17 @@ MUTATIONS = [
     ("online alpha sign flipped", "alpha = np.where(live, np.exp(m - m_new), 1.0)",
      "alpha = np.where(live, np.exp(m_new - m), 1.0)"),
     ("online sum uses no rescale", "l = l * alpha + p.sum(axis=1)", "l = l + p.sum(axis=1)"),
+    # rounding frame of the fp8 cast in the recurrence: against the previous running max (then
+    # rescaled into the new frame), or against the row's final max, instead of the running max
+    ("online rounds in the previous frame", "ph = p if rounder is None else rounder(p)",
+     "ph = p if rounder is None else rounder(p * np.exp(shift - np.where(np.isfinite(m), m, shift[:, 0])[:, None])) * np.exp(np.where(np.isfinite(m), m, shift[:, 0])[:, None] - shift)"),
+    ("online rounds in the final frame", "ph = p if rounder is None else rounder(p)",
+     "ph = p if rounder is None else rounder(p * np.exp(shift - np.where(vis_all, S_all, -np.inf).max(axis=1)[:, None])) * np.exp(np.where(vis_all, S_all, -np.inf).max(axis=1)[:, None] - shift)"),
+    ("online sum over the cast weights", "l = l * alpha + p.sum(axis=1)", "l = l * alpha + ph.sum(axis=1)"),
+    ("definition rounds the normalised weights", "Ph = P if rounder is None else rounder(P)",
+     "Ph = P if rounder is None else rounder(P / l) * l"),
+    ("definition sums the cast weights", "out[pos:pos + r.size] = (Ph @ v) / l",
+     "out[pos:pos + r.size] = (Ph @ v) / (Ph.sum(axis=1, keepdims=True) if rounder is not None else l)"),
 ]
 
 

@@ -5,15 +5,20 @@ with the source tree; nothing is installed elsewhere.  libattn_ceilings.so holds
 calibration kernels of the roofline (measured MFMA and HBM ceilings), not attention.
 """
 import os
+import shutil
 import subprocess
 import sys
 import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip"), os.path.join(HERE, "csrc", "attn_api.cpp")]
+# (source, extra flags): the e5m2-V instances keep their MFMA accumulators in VGPRs (the fp8
+# recurrence rescales O at every increase of a row maximum; see attn_fwd_v8.hip)
+SOURCES = [(os.path.join(HERE, "csrc", "attn_fwd.hip"), []),
+           (os.path.join(HERE, "csrc", "attn_fwd_v8.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+           (os.path.join(HERE, "csrc", "attn_api.cpp"), [])]
 LIBRARY = os.path.join(HERE, "libattn_fwd.so")
-CEILINGS_SOURCES = [os.path.join(HERE, "csrc", "ceilings.hip")]
+CEILINGS_SOURCES = [(os.path.join(HERE, "csrc", "ceilings.hip"), [])]
 CEILINGS_LIBRARY = os.path.join(HERE, "libattn_ceilings.so")
 # C++ host program that checks the C ABI without Python (links libattn_fwd.so)
 C_CHECK_SOURCE = os.path.join(HERE, "csrc", "c_abi_check.cpp")
@@ -24,7 +29,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # keep the compiler from forming packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # device code never produces NaN (masked scores are -inf, weights exp2(-inf) = 0), so
@@ -41,18 +45,45 @@ def hipcc():
     return "hipcc"
 
 
-def _start(sources, library, verbose, resource_report=None):
-    """Launch hipcc for one library into a temporary file; returns (process, tmp, library)."""
+def _compile(sources, library, verbose, resource_report=None):
+    """Compile each (source, flags) to an object (in parallel), then link LIBRARY.
+
+    Returns the error text, or None.  The library is replaced only when everything succeeded.
+    """
     stem = os.path.splitext(os.path.basename(library))[0]
-    fd, tmp = tempfile.mkstemp(prefix=f".{stem}.", suffix=".so.tmp", dir=HERE)
-    os.close(fd)
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + sources
-    if resource_report:
-        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
-    return proc, tmp, library
+    tmpdir = tempfile.mkdtemp(prefix=f".{stem}.", dir=HERE)
+    try:
+        procs = []
+        for src, extra in sources:
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [hipcc()] + HIPCC_FLAGS + extra + ["-c", "-o", obj, src]
+            if resource_report:
+                cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), obj))
+        outs, objs, failed = [], [], False
+        for proc, obj in procs:
+            out, err = proc.communicate()
+            outs.append(out + err)
+            objs.append(obj)
+            failed = failed or proc.returncode != 0
+        if resource_report:
+            with open(resource_report, "w") as f:
+                f.write("".join(outs))
+        if failed:
+            return "".join(outs)
+        tmp = os.path.join(tmpdir, os.path.basename(library))
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            return res.stdout + res.stderr
+        os.replace(tmp, library)
+        return None
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
 
 
 def build(verbose=False, resource_report=None):
@@ -61,23 +92,15 @@ def build(verbose=False, resource_report=None):
     resource_report: optional path; when given, the compiler's per-kernel register /
     LDS / occupancy remarks for LIBRARY are written there.
     """
-    jobs = [_start(SOURCES, LIBRARY, verbose, resource_report),
-            _start(CEILINGS_SOURCES, CEILINGS_LIBRARY, verbose)]
     failed = []
-    for i, (proc, tmp, library) in enumerate(jobs):
-        out, err = proc.communicate()
-        if i == 0 and resource_report:
-            with open(resource_report, "w") as f:
-                f.write(out + err)
-        if proc.returncode != 0:
-            os.unlink(tmp)
-            sys.stderr.write(out + err)
-            failed.append((library, proc.returncode))
-        else:
-            os.replace(tmp, library)
+    for sources, library, report in ((SOURCES, LIBRARY, resource_report),
+                                     (CEILINGS_SOURCES, CEILINGS_LIBRARY, None)):
+        err = _compile(sources, library, verbose, report)
+        if err is not None:
+            sys.stderr.write(err)
+            failed.append(os.path.basename(library))
     if failed:
-        raise RuntimeError("hipcc failed: " + ", ".join(f"{os.path.basename(l)} (status {c})"
-                                                        for l, c in failed))
+        raise RuntimeError("hipcc failed: " + ", ".join(failed))
     _build_c_check(verbose)
     return LIBRARY
 

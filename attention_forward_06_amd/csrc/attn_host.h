@@ -40,4 +40,7 @@ struct LaunchArgs {
 // HIP runtime's error code.  Implemented next to the kernels.
 int launch(const Problem& pr, const LaunchArgs& a, void* stream);
 
+// The same for the e5m2-V dtypes (their instances live in their own translation unit).
+int launch_v8(const Problem& pr, const LaunchArgs& a, void* stream);
+
 }  // namespace attn

@@ -837,6 +837,101 @@ void attn_fwd_kernel(Params p) {
     rescale_to(mx * p.c);
   };
 
+  // Unmasked iteration at head dim 256 with e5m2 V, as an explicit issue stream (one wave per
+  // SIMD: nothing else hides a late operand).  Score MFMA i (subtile i / DK, chunk i % DK) reads
+  // K fragment i, read NKA MFMAs ahead.  Each score MFMA carries one weight of P(t) (FMA,
+  // exponential, unrounded row sum); every fourth packs four weights to e5m2 (the P operand of
+  // the fp8 MFMAs), so the fp32 scores of S(t) are released as the pass goes.  The last score
+  // MFMAs issue the V^T reads of the first two fp8 P.V MFMAs; each P.V MFMA issues those two
+  // ahead, and carries two max3 steps of the row max of S(t+1); the reference then moves at
+  // every increase (the pages' fp8 recurrence) before the next iteration.
+  constexpr bool EXPL8 = D == 256 && C::V8 && MODE != kMaskBlock && KW == 64;
+  auto fast_iter_v8 = [&](int t, f32x16* s_cur, f32x16* s_nxt, const unsigned char* kb_nxt,
+                          const unsigned char* vb_cur, unsigned char* kb_dma, unsigned char* vb_dma) __attribute__((always_inline)) {
+    constexpr int NSM = 2 * C::DK;            // score MFMAs (32)
+    constexpr int NPM = C::DTL;               // fp8 P.V MFMAs (8), 64 keys each
+    constexpr int NKA = 4;                    // K fragments read ahead
+    constexpr int NVA = 2;                    // V^T fragments read ahead
+    static_assert(!EXPL8 || (NSM == 32 && NPM == 8), "issue stream shape");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t + 2 < ntiles) dma_k(key_begin + (t + 2) * BN, kb_dma);
+    if (t + 1 < ntiles) dma_v(key_begin + (t + 1) * BN, vb_dma);
+    auto kread = [&](int i) __attribute__((always_inline)) {
+      const int kt = i / C::DK, kk = i % C::DK;
+      return *(const u32x4*)(kb_nxt + k_lane_off + 32 * kt * C::KROWB + (((2 * kk + h) ^ kswz) << 4));
+    };
+    auto vread = [&](i32x8& a, int dt, int t4) __attribute__((always_inline)) {
+      const int row = 16 * t4 + tr8_row;
+      const int byte = 32 * dt + tr8_cb;
+      const int sw = ((byte >> 4) ^ swz_v<C::VROWB, true>(row)) << 4 | (byte & 15);
+      const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) i32x2*)(vb_cur + row * C::VROWB + sw));
+      a[2 * t4] = x[0];
+      a[2 * t4 + 1] = x[1];
+    };
+    u32x4 kf[NSM];
+    i32x8 vf[NPM];
+#pragma unroll
+    for (int i = 0; i < NKA; ++i) kf[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);
+    const float neg = -m_ref;
+    float psum = 0.f;
+    i32x8 pb;
+    f32x16 z0, z1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      z0[r] = 0.f;
+      z1[r] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NSM; ++i) {
+      if (i < C::DK) z0 = mfma_qk<C::QK>(kf[i], qf[i % C::DK], z0);
+      else z1 = mfma_qk<C::QK>(kf[i], qf[i % C::DK], z1);
+      const int j = i + NKA;
+      if (j < NSM) kf[j] = kread(j);
+      // V^T reads of P.V MFMAs 0 and 1 during the last eight score MFMAs
+      if (i >= NSM - 4 * NVA) vread(vf[(i - (NSM - 4 * NVA)) / 4], (i - (NSM - 4 * NVA)) / 4, (i - (NSM - 4 * NVA)) % 4);
+      // weight i of P(t): subtile i / 16, register i % 16
+      const int kt = i / 16, r = i % 16;
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kt][r], p.c, neg));
+      s_cur[kt][r] = e;
+      psum += e;
+      if ((r & 3) == 3) {
+        const int r4 = r - 3;
+        int word = __builtin_amdgcn_cvt_pk_bf8_f32(s_cur[kt][r4], s_cur[kt][r4 + 1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_bf8_f32(s_cur[kt][r4 + 2], s_cur[kt][r4 + 3], word, true);
+        pb[kt * 4 + r4 / 4] = word;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += psum;
+    s_nxt[0] = z0;
+    s_nxt[1] = z1;
+    __builtin_amdgcn_sched_barrier(0);
+    float mk[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int j = 0; j < NPM; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[j], pb, acc[j], 1, 1, 0, 0, 0, 0);
+      if (j + NVA < NPM) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) vread(vf[j + NVA], j + NVA, t4);
+      }
+      // two max3 steps of S(t+1) per P.V MFMA: subtile 0 first, subtile 1 (last score MFMA still
+      // running at the start) in the second half
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int step = 2 * j + q, kt = step / 8, r = 2 * (step % 8);
+        mk[kt] = max3(mk[kt], s_nxt[kt][r], s_nxt[kt][r + 1]);
+        asm("" : "+v"(mk[kt]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float mx = __builtin_fmaxf(mk[0], mk[1]);
+    mx = __builtin_fmaxf(mx, partner(mx));
+    rescale_to(mx * p.c);
+  };
+
   f32x16 sA[C::KT], sB[C::KT];
   if (ntiles > 0) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -847,7 +942,7 @@ void attn_fwd_kernel(Params p) {
     k_frags(fr0, lk0, live0, kswz);
     scores(sA, fr0, lk0, live0, kswz);
     // the explicit unmasked iterations expect the row max of their tile taken beforehand
-    if constexpr (EXPL) softmax_max(0, sA, live0, masked0);
+    if constexpr (EXPL || EXPL8) softmax_max(0, sA, live0, masked0);
   }
   int t = 0;
   // Unmasked iterations (tiles t and t+1 both unmasked) in pairs with fixed buffers.
@@ -855,6 +950,9 @@ void attn_fwd_kernel(Params p) {
     if constexpr (EXPL) {
       fast_iter_expl(t, sA, sB, lk1, lv0, lk0, lv1);
       fast_iter_expl(t + 1, sB, sA, lk0, lv1, lk1, lv0);
+    } else if constexpr (EXPL8) {
+      fast_iter_v8(t, sA, sB, lk1, lv0, lk0, lv1);
+      fast_iter_v8(t + 1, sB, sA, lk0, lv1, lk1, lv0);
     } else {
       iteration(true, t, sA, sB, lk1, lv0, lk0, lv1);
       iteration(true, t + 1, sB, sA, lk0, lv1, lk1, lv0);

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from attention_forward_06_amd import binding
-from attention_forward_06_amd.inputs import WORKLOADS, FUSED_PAGE_MATRIX, make_qkv, default_scale
+from attention_forward_06_amd.inputs import (WORKLOADS, FUSED_PAGE_MATRIX, make_qkv, default_scale,
+                                             storage_dtypes)
 
 from gpu_util import TOL, V8_DTYPES, gpu_qkv, run, sample_rows, to_f64
 
@@ -243,6 +244,46 @@ def test_sharp_rows_and_key_shift(mode, bs):
     ref2 = oracle.attn_ref(to_f64(q), to_f64(ks), to_f64(v), mode, default_scale(D), bs)
     assert float(np.abs(to_f64(o2) - ref2).max()) <= TOL["bf16"]
     assert float((o1.float() - o2.float()).abs().max()) <= 2 * TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["none", "causal"])
+@pytest.mark.parametrize("D,dtype", [(64, "f16"), (64, "bf16"), (128, "bf16"), (256, "bf16_v_e5m2")])
+@pytest.mark.parametrize("direction", [1, -1])
+def test_scores_growing_or_falling_along_the_keys(mode, D, dtype, direction):
+    # q_i = 4u and k_j = direction * 0.35 j u / |u|^2 (plus small noise): every score row moves by
+    # about 16 (base 2) per 64-key tile, up or down.  Growing rows force a new reference on every
+    # tile (the kernels' rare paths: the lazy reference's recomputation at D = 64, the rescale of
+    # the accumulator elsewhere); falling rows keep the first tile's reference while the weights
+    # of later tiles underflow.  Both against the fp64 definition.
+    L = 1024
+    g = torch.Generator().manual_seed(23)
+    u = torch.ones(D) / math.sqrt(D)
+    j = torch.arange(L, dtype=torch.float32)[:, None]
+    scale = 1.0 / math.sqrt(D)
+    step = 0.25 / (4 * scale * math.log2(math.e))   # score (base 2) change per key: 0.25
+    q = 4 * u + 0.05 * torch.randn(1, 1, L, D, generator=g)
+    k = direction * step * j * u + 0.05 * torch.randn(1, 1, L, D, generator=g)
+    v = torch.randn(1, 1, L, D, generator=g)
+    qd, kd, vd = storage_dtypes(dtype)
+    q, k, v = q.to(qd).cuda(), k.to(kd).cuda(), v.to(vd).cuda()
+    tag = f"{mode} D={D} {dtype} scores x{direction}"
+    if dtype not in V8_DTYPES:
+        _check(q, k, v, mode, 0, scale, dtype, tag)
+        return
+    # e5m2 P: here the pages' running-max rounding frame and the final-max frame of the plain
+    # definition (reading R1) differ by far more than on random inputs (a tile's predecessor
+    # still carries weight, rounded in an older frame).  Gate on the pages' recurrence with the
+    # kernel's 64-key tiles, and on R1 only beyond that recurrence's own distance from it.
+    o = run(q, k, v, mode, 0, scale)
+    qn, kn, vn, on = (to_f64(x) for x in (q, k, v, o))
+    rec = oracle.attn_online_ref(qn, kn, vn, mode, scale, 64, p_round="e5m2")
+    plain = oracle.attn_ref(qn, kn, vn, mode, scale, p_round="e5m2")
+    err_rec = float(np.abs(on - rec).max())
+    err_plain = float(np.abs(on - plain).max())
+    bar = max(TOL[dtype], float(np.abs(rec - plain).max()) + 2e-2)
+    _report(tag + " vs recurrence", err_rec, 2e-2)
+    _report(tag + " vs plain definition", err_plain, bar)
+    assert err_rec <= 2e-2 and err_plain <= bar
 
 
 @pytest.mark.parametrize("mode,D,dtype,bs", [("causal", 128, "bf16", 0), ("none", 64, "f16", 0),

@@ -12,10 +12,10 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-# (source, extra flags): the e5m2-V instances keep their MFMA accumulators in VGPRs (the fp8
-# recurrence rescales O at every increase of a row maximum; see attn_fwd_v8.hip)
+# (source, extra flags): the head-dim-256 instances keep their MFMA accumulators in VGPRs
+# (see attn_fwd_d256.hip)
 SOURCES = [(os.path.join(HERE, "csrc", "attn_fwd.hip"), []),
-           (os.path.join(HERE, "csrc", "attn_fwd_v8.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+           (os.path.join(HERE, "csrc", "attn_fwd_d256.hip"), ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
            (os.path.join(HERE, "csrc", "attn_api.cpp"), [])]
 LIBRARY = os.path.join(HERE, "libattn_fwd.so")
 CEILINGS_SOURCES = [(os.path.join(HERE, "csrc", "ceilings.hip"), [])]

@@ -1,6 +1,6 @@
-// Attention forward for AMD Instinct MI355X (gfx950): the instances with 16-bit V (all three
-// mask modes, head dims 16-256) and the host-side launch of a validated call.  The kernels are
-// in attn_kernel.h; the e5m2-V instances in attn_fwd_v8.hip.
+// Attention forward for AMD Instinct MI355X (gfx950): the instances of head dims 16-128 (none
+// and causal) and of block_diag, and the host-side launch of a validated call.  The kernels are
+// in attn_kernel.h; the head-dim-256 instances in attn_fwd_d256.hip.
 #include "attn_kernel.h"
 
 namespace {
@@ -44,8 +44,7 @@ hipError_t dispatch(const attn::Problem& pr, const Params& p, hipStream_t s) {
       return pr.dtype == kF16 ? dispatch_dense<128, kF16>(pr.mode, p, s)
                               : dispatch_dense<128, kBF16>(pr.mode, p, s);
     default:
-      if (pr.dtype == kF16) return dispatch_dense<256, kF16>(pr.mode, p, s);
-      return dispatch_dense<256, kBF16>(pr.mode, p, s);
+      return hipErrorInvalidValue;   // head dim 256: launch_d256
   }
 }
 
@@ -54,8 +53,8 @@ hipError_t dispatch(const attn::Problem& pr, const Params& p, hipStream_t s) {
 namespace attn {
 
 int launch(const Problem& pr, const LaunchArgs& a, void* stream) {
-  // e5m2 V: instances in attn_fwd_v8.hip
-  if (pr.dtype == kBF16V8 || pr.dtype == kF16V8) return launch_v8(pr, a, stream);
+  // head dim 256 (every dtype, none and causal): instances in attn_fwd_d256.hip
+  if (pr.mode != kMaskBlock && pr.D == 256) return launch_d256(pr, a, stream);
   return (int)dispatch(pr, make_params(a), (hipStream_t)stream);
 }
 

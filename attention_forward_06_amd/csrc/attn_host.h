@@ -40,7 +40,8 @@ struct LaunchArgs {
 // HIP runtime's error code.  Implemented next to the kernels.
 int launch(const Problem& pr, const LaunchArgs& a, void* stream);
 
-// The same for the e5m2-V dtypes (their instances live in their own translation unit).
-int launch_v8(const Problem& pr, const LaunchArgs& a, void* stream);
+// The same for head dim 256 in the streamed modes (its instances live in their own translation
+// unit, built with MFMA accumulators in VGPRs).
+int launch_d256(const Problem& pr, const LaunchArgs& a, void* stream);
 
 }  // namespace attn

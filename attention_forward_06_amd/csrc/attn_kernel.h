@@ -1,7 +1,7 @@
 // Attention forward kernels for gfx950, shared by the translation units that instantiate them:
-// attn_fwd.hip (16-bit V) and attn_fwd_v8.hip (OCP e5m2 V, built with MFMA accumulators in
-// VGPRs).  Everything here has internal linkage, so each unit holds its own instances and the
-// two sets never overlap.
+// attn_fwd.hip (head dims 16-128 and block_diag) and attn_fwd_d256.hip (head dim 256, built
+// with MFMA accumulators in VGPRs).  Everything here has internal linkage, so each unit holds
+// its own instances and the two sets never overlap.
 //
 // Fused scaled-dot-product attention forward for AMD Instinct MI355X (gfx950, CDNA4).
 //
@@ -722,22 +722,25 @@ void attn_fwd_kernel(Params p) {
     }
   };
 
-  // Unmasked iteration at head dim 128 with 16-bit P, written as an explicit issue stream.
+  // Unmasked iteration at head dims 128 and 256 with 16-bit P, written as an explicit issue
+  // stream.
   // Each group is one MFMA, the LDS reads of operands several MFMAs ahead, and a slice of VALU
   // work; a scheduling barrier closes each group, so the order below is the order issued.
   //   * score MFMA i (subtile i / DK, chunk i % DK) reads K fragment i, read NKA MFMAs ahead;
   //     the P.V MFMAs read V^T fragments NVA MFMAs ahead, the first ones during the last score
   //     MFMAs;
   //   * the exponentials of P(t) -- 16 pair-items (chunk cc, pair w: two FMAs, two
-  //     exponentials, one pack, one pair sum) -- are spread over the score MFMAs of S(t+1),
-  //     pipelined one group deep (exponentials of item k, pack and sum of item k - 1);
+  //     exponentials, one pack, one pair sum) -- are spread evenly over the score MFMAs of S(t+1)
+  //     (one per MFMA at D = 128, one every second MFMA at D = 256), pipelined one item deep
+  //     (exponentials of item k, pack and sum of item k - 1);
   //   * the row max of S(t+1) is spread over the P.V MFMAs (subtile 0 in the first half;
   //     subtile 1, whose last score MFMA is still running when P.V starts, in the second), and
   //     the reference moves (rarely) after them, so the next iteration starts with its
   //     exponentials.  The loop prologue takes the row max of tile 0.
   // A/B on one GPU against the compiler-scheduled iteration: +2% causal and +3% unmasked at
-  // D = 128; at D = 64 (half the MFMAs per exponential) it measured 3% slower and is not used.
-  constexpr bool EXPL = D == 128 && !C::V8 && MODE != kMaskBlock && C::KT == 2;
+  // D = 128; +31% causal and +16% unmasked at D = 256 (one wave per SIMD: nothing else hides a
+  // late operand there).  D = 64 has its own stream (lazy reference, below).
+  constexpr bool EXPL = (D == 128 || D == 256) && !C::V8 && MODE != kMaskBlock && C::KT == 2;
   auto fast_iter_expl = [&](int t, f32x16* s_cur, f32x16* s_nxt, const unsigned char* kb_nxt,
                             const unsigned char* vb_cur, unsigned char* kb_dma, unsigned char* vb_dma) __attribute__((always_inline)) {
     constexpr int NSM = 2 * C::DK;            // score MFMAs
@@ -745,9 +748,8 @@ void attn_fwd_kernel(Params p) {
     constexpr int NKA = 6;                    // K fragments read ahead
     constexpr int NVA = 4;                    // V^T fragments read ahead
     constexpr int NIT = (BN / 16) * 4;        // exponential pair-items
-    constexpr int IPM = NIT / NSM;            // items per score MFMA
     constexpr int NMX = 8;                    // max3 steps per 32-key subtile
-    static_assert(!EXPL || (NIT % NSM == 0 && NPM % 2 == 0 && NKA >= NVA), "issue stream shape");
+    static_assert(!EXPL || (NSM % NIT == 0 && NPM % 2 == 0 && NKA >= NVA), "issue stream shape");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t + 2 < ntiles) dma_k(key_begin + (t + 2) * BN, kb_dma);
@@ -802,9 +804,10 @@ void attn_fwd_kernel(Params p) {
       const int j = i + NKA;
       if (j < NSM) kf[j] = kread(j);
       else if (j - NSM < NPM) vf[j - NSM] = vread(j - NSM);
+      // item k rides on score MFMA (k * NSM) / NIT
 #pragma unroll
-      for (int q = 0; q < IPM; ++q) {
-        const int k = i * IPM + q;
+      for (int k = 0; k < NIT; ++k) {
+        if ((k * NSM) / NIT != i) continue;
         item_exp(k);
         if (k > 0) item_pack(k - 1);
       }

@@ -32,7 +32,7 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 HEADLINE = "causal_b4_h32_l4096_d128_bf16"
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_forward_06_amd", "csrc", f)
-                  for f in ("attn_kernel.h", "attn_fwd.hip", "attn_fwd_v8.hip")]
+                  for f in ("attn_kernel.h", "attn_fwd.hip", "attn_fwd_d256.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -414,7 +414,7 @@ def summarize_profiles(d):
                 if kname in r["Kernel_Name"] and int(r["Grid_Size_X"]) == grid]
         if not durs:
             continue
-        timed = 3 if "l32768" in n else 30
+        timed = 5 if "l32768" in n else 30
         t = durs[-timed:]
         lines.append(f"| `{kname}` | {n} | {len(durs)} | {sum(durs) / len(durs):.1f} | {min(durs):.1f} | "
                      f"{max(durs):.1f} | {sum(t) / len(t):.1f} ({len(t)} launches) |")
@@ -425,7 +425,7 @@ def summarize_profiles(d):
                 "Command (repo root, on one MI355X):\n\n```\n" + PROFILE_COMMANDS["prof_trace"] + "\n```\n\n"
                 f"Summarised by `python3 bench.py --summarize-profiles gpurun_out`; kernel source digest "
                 f"`{digest}`. All calls include the untimed warm-up launches (100, or 10 for L = 32768); "
-                "the last column averages only the launches bench.py times.\n\n"
+                "the last column averages only the launches bench.py times (with --steps 30: 30, or 5 for L = 32768).\n\n"
                 "| kernel | workload | calls | average (us) | min (us) | max (us) | timed launches: "
                 "average (us) |\n|---|---|---|---|---|---|---|\n" + "\n".join(lines) + "\n\n"
                 "Other kernels of the run (input generation, copies of sampled rows):\n\n"
@@ -510,10 +510,11 @@ def main():
         names = [a.only]
     res = {}
     for n in names:
-        # the L = 32768 launches are ~16x longer: a tenth of the launches, timed and warm-up
+        # the L = 32768 launches are ~13x longer than the headline's: a tenth of the launches,
+        # but at least 3 warm-up and 5 timed ones (context figures, not the timed step)
         long_seq = "l32768" in n
-        steps = max(1, a.steps // 10) if long_seq else a.steps
-        warmup = max(1, a.warmup // 10) if long_seq else a.warmup
+        steps = max(5, a.steps // 10) if long_seq else a.steps
+        warmup = max(3, a.warmup // 10) if long_seq else a.warmup
         res[n] = time_workload(n, steps, warmup)
         print(f"# {n}: {res[n]['ms']:.4f} ms/launch  {res[n]['tflops']:.1f} TFLOP/s  "
               f"{res[n]['gbs']:.1f} GB/s", file=sys.stderr, flush=True)

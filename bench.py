@@ -285,7 +285,8 @@ def cpu_baseline_workload(name, target_s):
             flops += 4 * D * visible_pairs(mode, L, bs)
             nbytes += L * D * (2 + 2 + vb + 2)
         units += 1
-    unit_name = "row subset of one (batch, head)" if extrapolated else "whole (batch, head) slices"
+    unit_name = ("row subsets, each of one (batch, head)," if extrapolated
+                 else "whole (batch, head) slices")
     if mode == "block_diag":
         value, unit = nbytes / elapsed / 1e9, "GB/s"
     else:

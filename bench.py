@@ -56,7 +56,7 @@ def parse():
                     help="skip the measured MFMA / HBM ceilings (e.g. under a counter profiler)")
     ap.add_argument("--summarize-profiles", metavar="DIR", default=None,
                     help="no GPU work: turn the rocprofv3 CSV output of the profiling passes under "
-                         "DIR (prof_trace, pmc_fetch, pmc_write, pmc_mfma, pmc_lds) into the "
+                         "DIR (prof_trace, pmc_fetch, pmc_write, pmc_mfma, pmc_lds; optionally the stall passes) into the "
                          "summaries in profiles/")
     return ap.parse_args()
 
@@ -319,6 +319,22 @@ PROFILE_COMMANDS = {
     "pmc_lds": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_MFMA "
                "SQ_WAVE_CYCLES GRBM_GUI_ACTIVE -d gpurun_out/pmc_lds -o run --output-format csv -- python3 "
                "bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-ceilings",
+    "pmc_stall_a": "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+                   "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_INST_LDS "
+                   "GRBM_GUI_ACTIVE -d gpurun_out/pmc_stall_a -o run --output-format csv -- python3 bench.py "
+                   "--steps 2 --warmup 1 --no-cpu-baseline --no-ceilings",
+    "pmc_stall_b": "rocprofv3 --pmc SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_MISC "
+                   "SQ_ACTIVE_INST_VALU2 SQ_IFETCH SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_BUSY_CU_CYCLES "
+                   "GRBM_GUI_ACTIVE -d gpurun_out/pmc_stall_b -o run --output-format csv -- python3 bench.py "
+                   "--steps 2 --warmup 1 --no-cpu-baseline --no-ceilings",
+    "pmc_icache": "rocprofv3 --pmc SQC_ICACHE_HITS SQC_ICACHE_MISSES SQC_ICACHE_MISSES_DUPLICATE SQC_ICACHE_REQ "
+                  "SQC_ICACHE_INPUT_VALID_READYB SQC_ICACHE_BUSY_CYCLES SQ_INSTS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE "
+                  "-d gpurun_out/pmc_icache -o run --output-format csv -- python3 bench.py --steps 2 --warmup 1 "
+                  "--no-cpu-baseline --no-ceilings",
+    "pmc_ldslat": "rocprofv3 --pmc LdsLatency -d gpurun_out/pmc_ldslat -o run --output-format csv -- python3 "
+                  "bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-ceilings",
+    "pmc_vmemlat": "rocprofv3 --pmc VmemLatency -d gpurun_out/pmc_vmemlat -o run --output-format csv -- python3 "
+                   "bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-ceilings",
 }
 DT_CODE = {"f16": 0, "bf16": 1, "bf16_v_e5m2": 2, "f16_v_e5m2": 3}
 MODE_CODE = {"none": 0, "causal": 1, "block_diag": 2}
@@ -480,7 +496,65 @@ def summarize_profiles(d):
                 "| workload | GUI clocks | MFMA busy | MFMA FLOPs issued / algorithmic | FLOP per clock per "
                 "SIMD (16-bit / fp8) | LDS busy | LDS bank conflicts | VALU instr per MFMA | LDS instr per "
                 "MFMA |\n|---|---|---|---|---|---|---|---|---|\n" + "\n".join(lines) + "\n")
+    if all(os.path.isdir(os.path.join(d, x)) for x in STALL_PASSES):
+        summarize_stalls(d, digest)
     print(f"wrote profiles/ from {d}", flush=True)
+
+
+STALL_PASSES = ("pmc_stall_a", "pmc_stall_b", "pmc_icache", "pmc_ldslat", "pmc_vmemlat")
+
+
+def summarize_stalls(d, digest):
+    """Where a wave's cycles go: issue, waits for issue, waits on dependencies, per workload."""
+    names = {"pmc_stall_a": ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                             "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_VALU_MFMA_COEXEC_CYCLES",
+                             "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE"),
+             "pmc_stall_b": ("SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_MISC"),
+             "pmc_icache": ("SQC_ICACHE_MISSES", "SQC_ICACHE_REQ", "SQ_INSTS", "SQ_WAVE_CYCLES"),
+             "pmc_ldslat": ("LdsLatency",), "pmc_vmemlat": ("VmemLatency",)}
+    tab = {(pas, c): _counters(os.path.join(d, pas), c) for pas, cs in names.items() for c in cs}
+    mean = lambda pas, c, n: (lambda v: sum(v) / len(v) if v else float("nan"))(_lookup(tab[(pas, c)], n) or [])
+    lines = []
+    for n in BENCH_WORKLOADS:
+        gui = mean("pmc_stall_a", "GRBM_GUI_ACTIVE", n) / 8
+        if gui != gui:
+            continue
+        wc = mean("pmc_stall_a", "SQ_WAVE_CYCLES", n)      # quad-cycles summed over waves
+        fa = lambda c: mean("pmc_stall_a", c, n) / wc
+        fb = lambda c: mean("pmc_stall_b", c, n) / wc
+        insts = mean("pmc_icache", "SQ_INSTS", n) / (4 * mean("pmc_icache", "SQ_WAVE_CYCLES", n))
+        miss = mean("pmc_icache", "SQC_ICACHE_MISSES", n) / mean("pmc_icache", "SQC_ICACHE_REQ", n)
+        lines.append(f"| {n} | {4 * wc / gui / 1024:.2f} | {fa('SQ_ACTIVE_INST_ANY'):.2f} | "
+                     f"{fa('SQ_WAIT_INST_ANY'):.2f} | {fa('SQ_WAIT_ANY'):.2f} | {fa('SQ_ACTIVE_INST_VALU'):.2f} | "
+                     f"{fa('SQ_ACTIVE_INST_LDS'):.3f} | {fb('SQ_ACTIVE_INST_SCA'):.3f} | "
+                     f"{fb('SQ_ACTIVE_INST_VMEM'):.3f} | "
+                     f"{mean('pmc_stall_a', 'SQ_VALU_MFMA_COEXEC_CYCLES', n) / (gui * 1024):.2f} | "
+                     f"{insts:.3f} | {miss:.5f} | {mean('pmc_ldslat', 'LdsLatency', n):.0f} | "
+                     f"{mean('pmc_vmemlat', 'VmemLatency', n):.0f} |")
+    cmds = "\n".join(PROFILE_COMMANDS[x] for x in STALL_PASSES)
+    with open(os.path.join(ROOT, "profiles", "attn_fwd_issue_and_wait_counters_all_workloads.md"), "w") as f:
+        f.write("# Where the waves' cycles go: issue, waits for issue, waits on dependencies\n\n"
+                "Five runs (repo root, on one MI355X):\n\n```\n" + cmds + "\n```\n\n"
+                f"Summarised by `python3 bench.py --summarize-profiles gpurun_out`; kernel source digest "
+                f"`{digest}`. The SQ cycle counters count per wave in units of 4 cycles; every column "
+                "below except the last four is a fraction of the waves' resident cycles "
+                "(SQ_WAVE_CYCLES), so issue + waits can exceed 1 (a wave can wait on a dependency while "
+                "its last instruction executes).\n\n"
+                "* waves per SIMD = 4 x SQ_WAVE_CYCLES / (GUI x 1024), GUI = GRBM_GUI_ACTIVE / 8;\n"
+                "* issuing = SQ_ACTIVE_INST_ANY; waiting for issue (an instruction ready, its unit taken) = "
+                "SQ_WAIT_INST_ANY; waiting on dependencies (s_waitcnt, barrier, operand) = SQ_WAIT_ANY;\n"
+                "* VALU, LDS, scalar, vector memory: SQ_ACTIVE_INST_* by instruction class (VALU includes "
+                "MFMA issue);\n"
+                "* MFMA co-issue = cycles in which the MFMA pipe was busy and a VALU instruction issued, "
+                "per SIMD cycle;\n"
+                "* instructions per wave cycle = SQ_INSTS / (4 x SQ_WAVE_CYCLES); I-cache miss rate = "
+                "SQC_ICACHE_MISSES / SQC_ICACHE_REQ;\n"
+                "* LDS and vector-memory latency (cycles per instruction, rocprofv3's derived LdsLatency and "
+                "VmemLatency; the vector-memory instructions are the K/V DMA and the Q loads).\n\n"
+                "| workload | waves per SIMD | issuing | waiting for issue | waiting on dependencies | "
+                "VALU | LDS | scalar | vector memory | MFMA co-issue | instructions per wave cycle | "
+                "I-cache miss rate | LDS latency | vector-memory latency |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n" + "\n".join(lines) + "\n")
 
 
 def main():

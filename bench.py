@@ -195,7 +195,7 @@ def measured_ceilings():
                    "after 5 warm-up"}
 
 
-# Tolerances of the spec comparison (max abs error against the oracle, by V's type).
+# Tolerances of the comparison with the oracle (max abs error, by V's type).
 TOLERANCE = {"f16": 2e-3, "bf16": 1e-2, "bf16_v_e5m2": 5e-2, "f16_v_e5m2": 5e-2}
 
 
@@ -209,8 +209,8 @@ def oracle_threads():
 
 def parity(r):
     """Max |GPU - oracle| over the sampled rows of the first and last (batch, head), against the
-    plain definition (with P rounded to e5m2 where V is e5m2: the spec oracle of that
-    workload); for e5m2 V the error against exact P is reported too."""
+    plain definition (with P rounded to e5m2 where V is e5m2, the unnormalised weights in the
+    final-max frame); for e5m2 V the error against exact P is reported too."""
     import numpy as np
     import oracle
     from attention_forward_06_amd.inputs import default_scale
@@ -233,7 +233,7 @@ def parity(r):
     out = {"max_abs_err": err, "tol": TOLERANCE[r["dtype"]], "pass": err <= TOLERANCE[r["dtype"]],
            "compared": f"{len(smp['rows'])} rows x 2 heads (first/last 64 + 64 seeded random rows "
                        f"of (b,h) = {smp['heads'][0]} and {smp['heads'][1]})",
-           "oracle": "plain definition, fp64" + (", P rounded to e5m2 (reading R1)" if fp8 else "")}
+           "oracle": "plain definition, fp64" + (", P rounded to e5m2 in the final-max frame" if fp8 else "")}
     if fp8:
         out["max_abs_err_exact_p"] = err_exact
     return out

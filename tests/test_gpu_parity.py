@@ -271,9 +271,10 @@ def test_scores_growing_or_falling_along_the_keys(mode, D, dtype, direction):
         _check(q, k, v, mode, 0, scale, dtype, tag)
         return
     # e5m2 P: here the pages' running-max rounding frame and the final-max frame of the plain
-    # definition (reading R1) differ by far more than on random inputs (a tile's predecessor
+    # definition with the cast differ by far more than on random inputs (a tile's predecessor
     # still carries weight, rounded in an older frame).  Gate on the pages' recurrence with the
-    # kernel's 64-key tiles, and on R1 only beyond that recurrence's own distance from it.
+    # kernel's 64-key tiles, and on the plain definition only beyond that recurrence's own
+    # distance from it.
     o = run(q, k, v, mode, 0, scale)
     qn, kn, vn, on = (to_f64(x) for x in (q, k, v, o))
     rec = oracle.attn_online_ref(qn, kn, vn, mode, scale, 64, p_round="e5m2")

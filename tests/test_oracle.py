@@ -246,7 +246,7 @@ def test_online_rounding_uses_running_max_frame():
 
 
 def test_plain_definition_rounds_in_final_frame():
-    # R1: the plain definition with the cast rounds exp(S - m_final), divides by the uncast sum
+    # the plain definition with the cast rounds exp(S - m_final), divides by the uncast sum
     q, k, v = _frame_case()
     o = oracle.attn_ref(q, k, v, "none", 1.0, p_round="e5m2")
     assert abs(o[0, 0, 1, 0] - FINAL_FRAME_O) <= 1e-12

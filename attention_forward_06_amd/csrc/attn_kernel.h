@@ -34,7 +34,9 @@
 //     on v_mfma_f32_32x32x64_f8f6f4 with both operands in bf8 (e5m2) format; the row sum uses
 //     the unrounded fp32 P ("Fused Attention", _attn_fwd_inner fp8 branch).
 //   * 16-bit P: the accumulator is rescaled only when a row max outgrows its reference by more
-//     than 2^8, and O is normalised by the sum of the rounded weights P.V used (see Cfg).
+//     than 2^8, and O is normalised by the sum of the rounded weights P.V used (see Cfg); at head
+//     dim 64 the unmasked tiles take no row max at all unless a weight may exceed 2^12 (see
+//     fast_iter_lazy).
 //   * K/V tiles go HBM -> LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane, rows past L
 //     read as zero), double-buffered with one barrier per tile; a software pipeline keeps K one
 //     tile ahead of V so the score MFMAs of tile t+1 overlap the softmax of tile t.
@@ -185,9 +187,11 @@ struct Cfg {
   // The fp8 path keeps the pages' sum over the unrounded p (P is far coarser there).
   static constexpr bool HAT = !V8;
   static constexpr int WAVES_PER_EU = (D >= 256) ? 1 : 2;
-  // With two waves on a SIMD, the one in its MFMA stretch (S(t+1), the exponentials of P(t),
-  // P(t).V(t)) is raised above the other, which is then in its barrier / DMA / row-max stretch:
-  // the matrix core gets the shared issue port first.  With one wave per SIMD there is no rival.
+  // General (compiler-scheduled) iteration with two waves on a SIMD: the wave in its MFMA
+  // stretch (S(t+1), the exponentials of P(t), P(t).V(t)) is raised above the other, which is
+  // then in its barrier / DMA / row-max stretch, so the matrix core gets the shared issue port
+  // first.  The explicit unmasked streams mix both stretches in every wave and leave the
+  // priority alone.  With one wave per SIMD there is no rival.
   static constexpr bool PRIO = WAVES_PER_EU > 1;
   static_assert(BN % 32 == 0, "key tile is a whole number of 32-key subtiles");
   static_assert(!V8 || BN % 64 == 0, "fp8 P.V consumes 64 keys per MFMA");

@@ -1,8 +1,9 @@
 """CPU fp64 oracle for the fused scaled-dot-product attention forward pass.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or load
-this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
-``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the oracle
+leg of ``bench.py`` (``cpu_baseline``, ``cpu_baseline_by_workload`` and the
+``max_abs_err`` comparison, all skipped with ``--no-cpu-baseline``) use it.  It shares no code with the HIP
 library in ``attention_forward_06_amd/`` and imports nothing from it.
 
 Contents

@@ -376,10 +376,11 @@ def _lookup(table, name):
     return None
 
 
-def summarize_profiles(d):
-    """Write profiles/traffic.json and the three markdown summaries from rocprofv3 CSV output."""
+def summarize_profiles(d, out=None):
+    """Write traffic.json and the markdown summaries from the rocprofv3 CSV output under d into
+    out (default: profiles/ of the repository)."""
     from attention_forward_06_amd.inputs import WORKLOADS
-    prof = os.path.join(ROOT, "profiles")
+    prof = out or os.path.join(ROOT, "profiles")
     digest = source_digest()
     short = lambda k: k[k.index("attn_fwd_kernel"):k.index(">") + 1]
     # --- HBM traffic: FETCH_SIZE / WRITE_SIZE (KiB per dispatch), scaled by a 1 GiB copy
@@ -497,14 +498,14 @@ def summarize_profiles(d):
                 "SIMD (16-bit / fp8) | LDS busy | LDS bank conflicts | VALU instr per MFMA | LDS instr per "
                 "MFMA |\n|---|---|---|---|---|---|---|---|---|\n" + "\n".join(lines) + "\n")
     if all(os.path.isdir(os.path.join(d, x)) for x in STALL_PASSES):
-        summarize_stalls(d, digest)
-    print(f"wrote profiles/ from {d}", flush=True)
+        summarize_stalls(d, digest, prof)
+    print(f"wrote {prof} from {d}", flush=True)
 
 
 STALL_PASSES = ("pmc_stall_a", "pmc_stall_b", "pmc_icache", "pmc_ldslat", "pmc_vmemlat")
 
 
-def summarize_stalls(d, digest):
+def summarize_stalls(d, digest, prof):
     """Where a wave's cycles go: issue, waits for issue, waits on dependencies, per workload."""
     names = {"pmc_stall_a": ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
                              "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_VALU_MFMA_COEXEC_CYCLES",
@@ -532,7 +533,7 @@ def summarize_stalls(d, digest):
                      f"{insts:.3f} | {miss:.5f} | {mean('pmc_ldslat', 'LdsLatency', n):.0f} | "
                      f"{mean('pmc_vmemlat', 'VmemLatency', n):.0f} |")
     cmds = "\n".join(PROFILE_COMMANDS[x] for x in STALL_PASSES)
-    with open(os.path.join(ROOT, "profiles", "attn_fwd_issue_and_wait_counters_all_workloads.md"), "w") as f:
+    with open(os.path.join(prof, "attn_fwd_issue_and_wait_counters_all_workloads.md"), "w") as f:
         f.write("# Where the waves' cycles go: issue, waits for issue, waits on dependencies\n\n"
                 "Five runs (repo root, on one MI355X):\n\n```\n" + cmds + "\n```\n\n"
                 f"Summarised by `python3 bench.py --summarize-profiles gpurun_out`; kernel source digest "

@@ -1,7 +1,7 @@
 // The C ABI of the attention forward (include/attn_fwd.h): argument checks and the conversion
-// of a call into launch arguments.  Plain C++ with no HIP dependency: the kernels and their
-// launcher live in attn_fwd.hip behind attn::launch, so this file also builds on its own with
-// the host sanitizers.
+// of a call into launch arguments.  Plain C++ with no HIP dependency: the kernels (attn_kernel.h)
+// and their launch (attn_fwd.hip, attn_fwd_d256.hip) sit behind attn::launch, so this file also
+// builds on its own with the host sanitizers.
 #include <climits>
 #include <cstdint>
 

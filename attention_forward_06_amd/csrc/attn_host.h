@@ -1,6 +1,6 @@
 // Interface between the host-side argument checks (attn_api.cpp, plain C++ with no HIP
 // dependency, so it can also be built with the host sanitizers) and the kernel launcher
-// (attn_fwd.hip).  Not part of the public C ABI.
+// (attn_fwd.hip; head dim 256 in attn_fwd_d256.hip).  Not part of the public C ABI.
 #pragma once
 
 #include <cstdint>

@@ -1,7 +1,8 @@
 // Attention forward for AMD Instinct MI355X (gfx950): the instances of head dims 16-128 (none
-// and causal) and of block_diag, and the host-side launch of a validated call.  The kernels are
-// in attn_kernel.h and (head dim 64, none and causal) attn_kernel_rows64.h; the head-dim-256
-// instances in attn_fwd_d256.hip.
+// and causal) and of block_diag, and the host-side launch of a validated call.  Head dims 16-64
+// (none and causal) run attn_fwd_rows64_kernel (attn_kernel_rows64.h), head dim 128 and
+// block_diag attn_fwd_kernel (attn_kernel.h); the head-dim-256 instances are in
+// attn_fwd_d256.hip.
 #include "attn_kernel.h"
 #include "attn_kernel_rows64.h"
 
@@ -32,18 +33,19 @@ hipError_t dispatch(const attn::Problem& pr, const Params& p, hipStream_t s) {
     return pr.dtype == kF16 ? dispatch_block<128, kF16>(pr.block_size, p, s)
                             : dispatch_block<128, kBF16>(pr.block_size, p, s);
   }
+  // head dims 16-64: 64 query rows per wave (attn_kernel_rows64.h)
+  const bool causal = pr.mode == kMaskCausal;
+  const bool f16 = pr.dtype == kF16;
   switch (pr.D) {
     case 16:
-      return pr.dtype == kF16 ? dispatch_dense<16, kF16>(pr.mode, p, s)
-                              : dispatch_dense<16, kBF16>(pr.mode, p, s);
+      if (causal) return f16 ? launch_rows64<16, kF16, kMaskCausal>(p, s) : launch_rows64<16, kBF16, kMaskCausal>(p, s);
+      return f16 ? launch_rows64<16, kF16, kMaskNone>(p, s) : launch_rows64<16, kBF16, kMaskNone>(p, s);
     case 32:
-      return pr.dtype == kF16 ? dispatch_dense<32, kF16>(pr.mode, p, s)
-                              : dispatch_dense<32, kBF16>(pr.mode, p, s);
+      if (causal) return f16 ? launch_rows64<32, kF16, kMaskCausal>(p, s) : launch_rows64<32, kBF16, kMaskCausal>(p, s);
+      return f16 ? launch_rows64<32, kF16, kMaskNone>(p, s) : launch_rows64<32, kBF16, kMaskNone>(p, s);
     case 64:
-      // 64 query rows per wave (attn_kernel_rows64.h)
-      if (pr.mode == kMaskCausal)
-        return pr.dtype == kF16 ? launch_rows64<kF16, kMaskCausal>(p, s) : launch_rows64<kBF16, kMaskCausal>(p, s);
-      return pr.dtype == kF16 ? launch_rows64<kF16, kMaskNone>(p, s) : launch_rows64<kBF16, kMaskNone>(p, s);
+      if (causal) return f16 ? launch_rows64<64, kF16, kMaskCausal>(p, s) : launch_rows64<64, kBF16, kMaskCausal>(p, s);
+      return f16 ? launch_rows64<64, kF16, kMaskNone>(p, s) : launch_rows64<64, kBF16, kMaskNone>(p, s);
     case 128:
       return pr.dtype == kF16 ? dispatch_dense<128, kF16>(pr.mode, p, s)
                               : dispatch_dense<128, kBF16>(pr.mode, p, s);

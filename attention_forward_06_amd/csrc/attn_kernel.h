@@ -1,7 +1,8 @@
 // Attention forward kernels for gfx950, shared by the translation units that instantiate them:
-// attn_fwd.hip (head dims 16-128 and block_diag) and attn_fwd_d256.hip (head dim 256, built
-// with MFMA accumulators in VGPRs).  Everything here has internal linkage, so each unit holds
-// its own instances and the two sets never overlap.
+// attn_fwd.hip (head dim 128 and block_diag) and attn_fwd_d256.hip (head dim 256, built with
+// MFMA accumulators in VGPRs).  Head dims 16-64 (none and causal) run attn_fwd_rows64_kernel
+// (attn_kernel_rows64.h), built on the helpers here.  Everything here has internal linkage, so
+// each unit holds its own instances and the two sets never overlap.
 //
 // Fused scaled-dot-product attention forward for AMD Instinct MI355X (gfx950, CDNA4).
 //
@@ -34,14 +35,12 @@
 //     on v_mfma_f32_32x32x64_f8f6f4 with both operands in bf8 (e5m2) format; the row sum uses
 //     the unrounded fp32 P ("Fused Attention", _attn_fwd_inner fp8 branch).
 //   * 16-bit P: the accumulator is rescaled only when a row max outgrows its reference by more
-//     than 2^8, and O is normalised by the sum of the rounded weights P.V used (see Cfg); at head
-//     dim 64 the unmasked tiles take no row max at all unless a weight may exceed 2^12 (see
-//     fast_iter_lazy).
+//     than 2^8, and O is normalised by the sum of the rounded weights P.V used (see Cfg).
 //   * K/V tiles go HBM -> LDS by LDS-DMA (buffer_load ... lds, 16 bytes per lane, rows past L
 //     read as zero), double-buffered with one barrier per tile; a software pipeline keeps K one
 //     tile ahead of V so the score MFMAs of tile t+1 overlap the softmax of tile t.
-//   * Any layout with a contiguous head dim (per-tensor batch / head / row strides); head dim 16
-//     runs the head-dim-32 tiles with zero upper halves.
+//   * Any layout with a contiguous head dim (per-tensor batch / head / row strides); a head dim
+//     of 16 (Cfg) runs head-dim-32 tiles with zero upper halves.
 //   * Workgroup ids are remapped so all query blocks of one (batch, head) land on the same
 //     XCD (its K/V stays in that XCD's L2); causal blocks run longest first within small head
 //     groups, so the CUs of an XCD finish together.
@@ -743,7 +742,7 @@ void attn_fwd_kernel(Params p) {
   //     exponentials.  The loop prologue takes the row max of tile 0.
   // A/B on one GPU against the compiler-scheduled iteration: +2% causal and +3% unmasked at
   // D = 128; +31% causal and +16% unmasked at D = 256 (one wave per SIMD: nothing else hides a
-  // late operand there).  D = 64 has its own stream (lazy reference, below).
+  // late operand there).
   constexpr bool EXPL = (D == 128 || D == 256) && !C::V8 && MODE != kMaskBlock && C::KT == 2;
   auto fast_iter_expl = [&](int t, f32x16* s_cur, f32x16* s_nxt, const unsigned char* kb_nxt,
                             const unsigned char* vb_cur, unsigned char* kb_dma, unsigned char* vb_dma) __attribute__((always_inline)) {
@@ -939,134 +938,6 @@ void attn_fwd_kernel(Params p) {
     rescale_to(mx * p.c);
   };
 
-  // Unmasked iteration at head dim 64 with 16-bit P, as an explicit issue stream with a lazy
-  // reference.  At D = 64 the softmax work per score meets half the MFMA work of D = 128, and
-  // the row max alone measured 13% of the time, so the unmasked iteration takes no row max:
-  // P(t) is computed against the reference as it stands, and only when some lane's tile sum of
-  // the rounded weights exceeds SUM_CAP (so one weight may have) does the wave take the exact
-  // row max, move the reference to it at any increase, and recompute P(t).  Weights stay below
-  // SUM_CAP = 2^12, far inside binary16 and bfloat16; the result is exact in real arithmetic for
-  // any reference (O = sum P^ v / sum P^ in one common frame).  K fragments are read NKA MFMAs
-  // ahead, V^T fragments NVA ahead; two exponential pair-items ride on each score MFMA.
-  constexpr bool EXPLZ = D == 64 && !C::V8 && MODE != kMaskBlock && C::KT == 2;
-  constexpr float SUM_CAP = 4096.f;
-  auto fast_iter_lazy = [&](int t, f32x16* s_cur, f32x16* s_nxt, const unsigned char* kb_nxt,
-                            const unsigned char* vb_cur, unsigned char* kb_dma, unsigned char* vb_dma) __attribute__((always_inline)) {
-    constexpr int NSM = 2 * C::DK;            // score MFMAs (8)
-    constexpr int NPM = (BN / 16) * C::DTL;   // P.V MFMAs (8)
-    constexpr int NKA = 4;                    // K fragments read ahead
-    constexpr int NVA = 4;                    // V^T fragments read ahead
-    constexpr int NIT = (BN / 16) * 4;        // exponential pair-items (16)
-    constexpr int IPM = NIT / NSM;            // items per score MFMA (2)
-    static_assert(!EXPLZ || (NIT % NSM == 0 && NKA >= NVA), "issue stream shape");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (t + 2 < ntiles) dma_k(key_begin + (t + 2) * BN, kb_dma);
-    if (t + 1 < ntiles) dma_v(key_begin + (t + 1) * BN, vb_dma);
-    auto kread = [&](int i) __attribute__((always_inline)) {
-      const int kt = i / C::DK, kk = i % C::DK;
-      return *(const u32x4*)(kb_nxt + k_lane_off + 32 * kt * C::KROWB + (((2 * kk + h) ^ kswz) << 4));
-    };
-    auto vread = [&](int j) __attribute__((always_inline)) {
-      const int cc = j / C::DTL, dt = j % C::DTL;
-      u32x4 a;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int row = 16 * cc + 4 * tt + tr16_row;
-        const int byte = 64 * dt + tr16_cb;
-        const int sw = ((byte >> 4) ^ swz_v<C::VROWB, false>(row)) << 4 | (byte & 15);
-        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(vb_cur + row * C::VROWB + sw));
-        __builtin_memcpy((char*)&a + 8 * tt, &x, 8);
-      }
-      return a;
-    };
-    u32x4 kf[NSM], vf[NPM];
-#pragma unroll
-    for (int i = 0; i < NKA; ++i) kf[i] = kread(i);
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 pk[BN / 16];
-    float lh = 0.f, le = 0.f;
-    float e0[NIT], e1[NIT];
-    auto item_exp = [&](int k, float neg) __attribute__((always_inline)) {
-      const int cc = k >> 2, w = k & 3, kt = cc >> 1, c8 = (cc & 1) * 8;
-      e0[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kt][c8 + 2 * w], p.c, neg));
-      e1[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kt][c8 + 2 * w + 1], p.c, neg));
-    };
-    auto item_pack = [&](int k) __attribute__((always_inline)) {
-      const int cc = k >> 2, w = k & 3;
-      pk[cc][w] = pack2<DT>(e0[k], e1[k]);
-      lh = sum2_acc<DT>(pk[cc][w], lh);
-      if constexpr (LSE) le += e0[k] + e1[k];
-    };
-    f32x16 z0, z1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      z0[r] = 0.f;
-      z1[r] = 0.f;
-    }
-    const float neg0 = -m_ref;
-#pragma unroll
-    for (int i = 0; i < NSM; ++i) {
-      if (i < C::DK) z0 = mfma_qk<C::QK>(kf[i], qf[i % C::DK], z0);
-      else z1 = mfma_qk<C::QK>(kf[i], qf[i % C::DK], z1);
-      const int j = i + NKA;
-      if (j < NSM) kf[j] = kread(j);
-      else if (j - NSM < NPM) vf[j - NSM] = vread(j - NSM);
-#pragma unroll
-      for (int q = 0; q < IPM; ++q) {
-        const int k = i * IPM + q;
-        item_exp(k, neg0);
-        if (k > 0) item_pack(k - 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    item_pack(NIT - 1);
-    s_nxt[0] = z0;
-    s_nxt[1] = z1;
-    // rare: a weight may exceed the cap -- exact row max, reference moved, P(t) again
-    if (__builtin_amdgcn_ballot_w64(lh > SUM_CAP)) {
-      float mk[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mk[kt] = max3(mk[kt], s_cur[kt][r], s_cur[kt][r + 1]);
-      float mx = __builtin_fmaxf(mk[0], mk[1]);
-      mx = __builtin_fmaxf(mx, partner(mx)) * p.c;
-      const bool up = mx > m_ref;
-      if (__builtin_amdgcn_ballot_w64(up)) {
-        const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
-        m_ref = up ? mx : m_ref;
-        l_run *= alpha;
-        l_hat *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::DTL; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      }
-      lh = 0.f;
-      le = 0.f;
-#pragma unroll
-      for (int k = 0; k < NIT; ++k) {
-        item_exp(k, -m_ref);
-        item_pack(k);
-      }
-    }
-    l_hat += lh;
-    if constexpr (LSE) l_run += le;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = NKA; j < NVA; ++j) vf[j] = vread(j);
-#pragma unroll
-    for (int j = 0; j < NPM; ++j) {
-      const int cc = j / C::DTL, dt = j % C::DTL;
-      acc[dt] = mfma_qk<DT>(vf[j], pk[cc], acc[dt]);
-      const int jn = j + NVA;
-      if (jn < NPM) vf[jn] = vread(jn);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
   f32x16 sA[C::KT], sB[C::KT];
   if (ntiles > 0) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -1077,7 +948,7 @@ void attn_fwd_kernel(Params p) {
     k_frags(fr0, lk0, live0, kswz);
     scores(sA, fr0, lk0, live0, kswz);
     // the explicit unmasked iterations expect the row max of their tile taken beforehand
-    if constexpr (EXPL || EXPL8 || EXPLZ) softmax_max(0, sA, live0, masked0);
+    if constexpr (EXPL || EXPL8) softmax_max(0, sA, live0, masked0);
   }
   int t = 0;
   // Unmasked iterations (tiles t and t+1 both unmasked) in pairs with fixed buffers.
@@ -1088,9 +959,6 @@ void attn_fwd_kernel(Params p) {
     } else if constexpr (EXPL8) {
       fast_iter_v8(t, sA, sB, lk1, lv0, lk0, lv1);
       fast_iter_v8(t + 1, sB, sA, lk0, lv1, lk1, lv0);
-    } else if constexpr (EXPLZ) {
-      fast_iter_lazy(t, sA, sB, lk1, lv0, lk0, lv1);
-      fast_iter_lazy(t + 1, sB, sA, lk0, lv1, lk1, lv0);
     } else {
       iteration(true, t, sA, sB, lk1, lv0, lk0, lv1);
       iteration(true, t + 1, sB, sA, lk0, lv1, lk1, lv0);

@@ -1,17 +1,17 @@
-// Head dim 64, none and causal, 16-bit V: 64 query rows per wave.
+// Head dims 16, 32 and 64, none and causal, 16-bit V: 64 query rows per wave.
 //
 // Same online softmax as attn_fwd_kernel ("Triton-CUDA Attention", online-softmax core;
 // "Fused Attention", _attn_fwd_inner: running max, running sum, rescaled accumulator, O = acc / l),
 // same operand layouts (S^T = K * Q^T with the key permutation pi, O^T = V^T * P^T with
 // transposing V reads), same LDS-DMA tile staging.  What differs is the work of one wave: two
 // groups of 32 query rows (row group r holds rows qw0 + 32 r + lane % 32), so every K fragment and
-// every V^T fragment read from LDS feeds two MFMAs instead of one.  At head dim 64 one SIMD
+// every V^T fragment read from LDS feeds two MFMAs instead of one.  At these head dims one SIMD
 // issuing the MFMAs, their LDS operand reads and the softmax VALU work of two waves is what bounds
-// the 32-row kernel; halving the LDS reads per MFMA moves that bound.  Registers: Q fragments
-// 2 x 16, accumulators 2 x 32, scores 2 x 32, K or V^T fragments 32 -- two waves per SIMD still
-// fit.
+// the 32-row kernel; halving the LDS reads per MFMA moves that bound.  Registers at head dim 64:
+// Q fragments 2 x 16, accumulators 2 x 32, scores 2 x 32, K or V^T fragments 32 -- two waves per
+// SIMD still fit; head dim 16 fits three.
 //
-// Per key tile (64 keys) and wave, the unmasked iteration issues four phases of 8 MFMAs:
+// Per key tile (64 keys) and wave, the unmasked iteration issues four phases of MFMAs:
 //   A  scores of row group 0 (K fragments read once, kept),
 //   B  scores of row group 1 from the same K fragments, while the VALU exponentiates row
 //      group 0's weights,
@@ -20,24 +20,27 @@
 //   D  P.V of row group 1 from the same V^T fragments.
 // Tiles are not pipelined across iterations (the second row group gives each phase's VALU work
 // MFMAs to hide under); K and V of tile t+1 stream into the other LDS buffer during tile t.
-// The unmasked iteration keeps the lazy reference of the 32-row head-dim-64 kernel: no row max
-// unless a tile's sum of rounded weights exceeds SUM_CAP in some row (exact in real arithmetic
-// for any reference).  The causal diagonal and a ragged tail take the general iteration (mask,
-// row max, capped rescale), one row group after the other.
+// The unmasked iteration takes no row max unless a tile's sum of rounded weights exceeds
+// SUM_CAP in some row (a lazy reference, exact in real arithmetic for any reference).  The causal
+// diagonal and a ragged tail take the general iteration (mask, row max, capped rescale), one row
+// group after the other.  Head dim 16 runs 32-wide tiles whose upper half is zero (as
+// attn_fwd_kernel does); its score MFMAs skip that half.
 #pragma once
 
 #include "attn_kernel.h"
 
 namespace {
 
-template <int DT, int MODE, bool LSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int DT, int MODE, bool LSE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 16 ? 3 : 2)))
 void attn_fwd_rows64_kernel(Params p) {
-  constexpr int D = 64, NW = 4, BN = 64, RG = 2;
+  constexpr int NW = 4, BN = 64, RG = 2;
   using C = Cfg<D, DT, MODE, NW, BN>;   // tile, DMA and swizzle constants (C::BM is not this kernel's)
   constexpr int BM = 64 * NW;           // query rows per workgroup
-  constexpr int DK = C::DK, DTL = C::DTL;
-  static_assert(!C::V8 && MODE != kMaskBlock && C::KT == 2 && DK == 4 && DTL == 2, "head dim 64, 16-bit");
+  // DK: 16-wide d chunks holding data (head dim 16 runs 32-wide tiles whose upper half is zero;
+  // its score MFMAs skip that half)
+  constexpr int DK = (D + 15) / 16, DTL = C::DTL;
+  static_assert(!C::V8 && MODE != kMaskBlock && C::KT == 2 && D <= 64, "head dim 16-64, 16-bit");
   __shared__ __attribute__((aligned(1024))) unsigned char lk0[C::KTILE];
   __shared__ __attribute__((aligned(1024))) unsigned char lv0[C::VTILE];
   __shared__ __attribute__((aligned(1024))) unsigned char lk1[C::KTILE];
@@ -67,7 +70,9 @@ void attn_fwd_rows64_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, k_oob);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, v_oob);
 
-  // LDS-DMA lane offsets, as in attn_fwd_kernel (head dim 64 has no padded chunks).
+  // LDS-DMA lane offsets, as in attn_fwd_kernel (the chunks of a padded row, D = 16, point past
+  // the buffer and read as zeros).
+  constexpr unsigned kPadOff = 0x80000000u;
   unsigned k_off[C::KPER], v_off[C::VPER];
 #pragma unroll
   for (int i = 0; i < C::KPER; ++i) {
@@ -75,7 +80,7 @@ void attn_fwd_rows64_kernel(Params p) {
     const int row = byte / C::KROWB;
     const int lch = ((byte % C::KROWB) >> 4) ^ swz_k<C::KROWB>(row);
     const int rin = (wave * 1024 + lane * 16) / C::KROWB;
-    k_off[i] = (unsigned)(rin * k_rs + lch * 16);
+    k_off[i] = lch * 16 < C::KGROWB ? (unsigned)(rin * k_rs + lch * 16) : kPadOff;
   }
 #pragma unroll
   for (int i = 0; i < C::VPER; ++i) {
@@ -83,7 +88,7 @@ void attn_fwd_rows64_kernel(Params p) {
     const int row = byte / C::VROWB;
     const int lch = ((byte % C::VROWB) >> 4) ^ swz_v<C::VROWB, false>(row);
     const int rin = (wave * 1024 + lane * 16) / C::VROWB;
-    v_off[i] = (unsigned)(rin * v_rs + lch * 16);
+    v_off[i] = lch * 16 < C::VGROWB ? (unsigned)(rin * v_rs + lch * 16) : kPadOff;
   }
   auto dma_k = [&](int key0, unsigned char* kb) __attribute__((always_inline)) {
     if (key0 + BN <= L) dma_rows<C::KROWB, C::KDMA, C::KPER, NW, BN>(rk, key0, L, k_rs, wave, lane, k_oob, k_off, kb, true);
@@ -112,7 +117,8 @@ void attn_fwd_rows64_kernel(Params p) {
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk) {
       const int q = qw0 + 32 * r + col;
-      const unsigned off = q < L ? (unsigned)(q * q_rs + (16 * kk + 8 * h) * 2) : q_ext;
+      const bool in = q < L && 16 * kk + 8 * h < D;   // d >= D: the zero half of a padded row
+      const unsigned off = in ? (unsigned)(q * q_rs + (16 * kk + 8 * h) * 2) : q_ext;
       qf[r][kk] = buf_load16(rq, off);
     }
 
@@ -261,18 +267,21 @@ void attn_fwd_rows64_kernel(Params p) {
 
   // Unmasked iteration: the four phases of the header comment, each MFMA closing a scheduling
   // group with its share of LDS reads and VALU work.  Exponential pair-item k of a row group
-  // (chunk k / 4, pair k % 4: two FMAs, two exponentials, one pack, one pair sum) is issued two
-  // per MFMA, pipelined one deep (exponentials of item k, pack and sum of item k - 1).
+  // (chunk k / 4, pair k % 4: two FMAs, two exponentials, one pack, one pair sum) rides on the
+  // MFMAs of phase B (row group 0) or C (row group 1), spread evenly, pipelined one deep
+  // (exponentials of item k, pack and sum of item k - 1).  A tile sum of at most SUM_CAP = 2^12
+  // bounds every weight far inside binary16 and bfloat16.
   constexpr float SUM_CAP = 4096.f;
   auto fast = [&](int t, const unsigned char* kb, const unsigned char* vb, unsigned char* kb_dma,
                   unsigned char* vb_dma) __attribute__((always_inline)) {
     constexpr int NS = 2 * DK;            // score MFMAs per row group (8)
     constexpr int NP = (BN / 16) * DTL;   // P.V MFMAs per row group (8)
-    constexpr int NKA = 4;                // K fragments read ahead
-    constexpr int NVA = 4;                // V^T fragments read ahead
+    constexpr int NKA = NS < 4 ? NS : 4;  // K fragments read ahead
+    constexpr int NVA = NS < 4 ? NS : 4;  // V^T fragments read ahead
     constexpr int NIT = (BN / 16) * 4;    // pair-items per row group (16)
-    constexpr int IPM = NIT / NS;         // pair-items per MFMA (2)
-    static_assert(NIT == IPM * NS && NIT == IPM * NP && NVA <= NS, "issue stream shape");
+    constexpr int IPB = NIT / NS;         // pair-items per score MFMA of phase B
+    constexpr int IPC = NIT / NP;         // pair-items per P.V MFMA of phase C
+    static_assert(NIT == IPB * NS && NIT == IPC * NP && NVA <= NS, "issue stream shape");
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (t + 1 < ntiles) {
@@ -352,8 +361,8 @@ void attn_fwd_rows64_kernel(Params p) {
         vf[j] = vread(vb, j / DTL, j % DTL);
       }
 #pragma unroll
-      for (int q = 0; q < IPM; ++q) {
-        const int k = i * IPM + q;
+      for (int q = 0; q < IPB; ++q) {
+        const int k = i * IPB + q;
         item_exp(0, k, neg0);
         if (k > 0) item_pack(0, k - 1);
       }
@@ -369,8 +378,8 @@ void attn_fwd_rows64_kernel(Params p) {
       acc[0][j % DTL] = mfma_qk<DT>(vf[j], pk[0][j / DTL], acc[0][j % DTL]);
       if (j + NVA < NP) vf[j + NVA] = vread(vb, (j + NVA) / DTL, (j + NVA) % DTL);
 #pragma unroll
-      for (int q = 0; q < IPM; ++q) {
-        const int k = j * IPM + q;
+      for (int q = 0; q < IPC; ++q) {
+        const int k = j * IPC + q;
         item_exp(1, k, neg1);
         if (k > 0) item_pack(1, k - 1);
       }
@@ -419,6 +428,7 @@ void attn_fwd_rows64_kernel(Params p) {
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           // registers 4 a4 .. 4 a4 + 3 hold d = 32 dt + 8 a4 + 4 h + 0..3
+          if (32 * dt + 8 * a4 >= D) continue;      // padded head dim: nothing to store
           u32x2 w;
           w[0] = pack2<C::QK>(acc[r][dt][4 * a4] * inv, acc[r][dt][4 * a4 + 1] * inv);
           w[1] = pack2<C::QK>(acc[r][dt][4 * a4 + 2] * inv, acc[r][dt][4 * a4 + 3] * inv);
@@ -430,9 +440,9 @@ void attn_fwd_rows64_kernel(Params p) {
 }
 
 // Launch of the 64-rows-per-wave kernel: 256 query rows per workgroup.
-template <int DT, int MODE>
+template <int D, int DT, int MODE>
 hipError_t launch_rows64(const Params& p0, hipStream_t stream) {
-  constexpr int BM = 256, D = 64;
+  constexpr int BM = 256;
   Params p = p0;
   p.n_qblocks = (p.L + BM - 1) / BM;
   const long long blocks = (long long)p.n_qblocks * p.bh;
@@ -448,9 +458,9 @@ hipError_t launch_rows64(const Params& p0, hipStream_t stream) {
       }
   }
   if (p.lse != nullptr)
-    hipLaunchKernelGGL((attn_fwd_rows64_kernel<DT, MODE, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_rows64_kernel<D, DT, MODE, true>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((attn_fwd_rows64_kernel<DT, MODE, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_rows64_kernel<D, DT, MODE, false>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

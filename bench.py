@@ -344,9 +344,9 @@ def kernel_of(name):
     """(kernel name as rocprofv3 prints it, grid size in work-items) of a bench workload."""
     from attention_forward_06_amd.inputs import WORKLOADS
     w = WORKLOADS[name]
-    if w["D"] == 64 and w["mode"] in ("none", "causal"):
-        # head dim 64, none and causal: 64 query rows per wave, 256 per workgroup
-        kname = f"attn_fwd_rows64_kernel<{DT_CODE[w['dtype']]}, {MODE_CODE[w['mode']]}, false>"
+    if w["D"] <= 64 and w["mode"] in ("none", "causal"):
+        # head dims 16-64, none and causal: 64 query rows per wave, 256 per workgroup
+        kname = f"attn_fwd_rows64_kernel<{w['D']}, {DT_CODE[w['dtype']]}, {MODE_CODE[w['mode']]}, false>"
         return kname, -(-w["L"] // 256) * w["B"] * w["H"] * 256
     bn, kw = (128, w["block_size"]) if w["mode"] == "block_diag" else (64, 64)
     kname = (f"attn_fwd_kernel<{w['D']}, {DT_CODE[w['dtype']]}, {MODE_CODE[w['mode']]}, 4, {bn}, {kw}, "

@@ -451,9 +451,11 @@ def summarize_profiles(d, out=None):
                 "average (us) |\n|---|---|---|---|---|---|---|\n" + "\n".join(lines) + "\n\n"
                 "Other kernels of the run (input generation, copies of sampled rows):\n\n"
                 "| kernel | calls | average (us) |\n|---|---|---|\n" + "\n".join(others) + "\n\n"
-                "Template arguments: <head dim, dtype (0 f16, 1 bf16, 2 bf16 with e5m2 V, 3 f16 with e5m2 "
-                "V), mask (0 none, 1 causal, 2 block_diag), waves per workgroup, keys per tile, keys per "
-                "wave, writes the log-normaliser>.\n")
+                "Template arguments: attn_fwd_kernel<head dim, dtype (0 f16, 1 bf16, 2 bf16 with e5m2 V, "
+                "3 f16 with e5m2 V), mask (0 none, 1 causal, 2 block_diag), waves per workgroup, keys per "
+                "tile, keys per wave, writes the log-normaliser>; attn_fwd_rows64_kernel<head dim, dtype, "
+                "mask, writes the log-normaliser> (64 query rows per wave, 4 waves per workgroup, 64-key "
+                "tiles).\n")
     # --- MFMA and LDS counters
     mf = {c: _counters(os.path.join(d, "pmc_mfma"), c) for c in
           ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",

@@ -247,12 +247,13 @@ def test_sharp_rows_and_key_shift(mode, bs):
 
 
 @pytest.mark.parametrize("mode", ["none", "causal"])
-@pytest.mark.parametrize("D,dtype", [(64, "f16"), (64, "bf16"), (128, "bf16"), (256, "bf16_v_e5m2")])
+@pytest.mark.parametrize("D,dtype", [(16, "bf16"), (32, "f16"), (64, "f16"), (64, "bf16"), (128, "bf16"),
+                                     (256, "bf16_v_e5m2")])
 @pytest.mark.parametrize("direction", [1, -1])
 def test_scores_growing_or_falling_along_the_keys(mode, D, dtype, direction):
     # q_i = 4u and k_j = direction * 0.35 j u / |u|^2 (plus small noise): every score row moves by
     # about 16 (base 2) per 64-key tile, up or down.  Growing rows force a new reference on every
-    # tile (the kernels' rare paths: the lazy reference's recomputation at D = 64, the rescale of
+    # tile (the kernels' rare paths: the lazy reference's recomputation at D <= 64, the rescale of
     # the accumulator elsewhere); falling rows keep the first tile's reference while the weights
     # of later tiles underflow.  Both against the fp64 definition.
     L = 1024
@@ -288,6 +289,7 @@ def test_scores_growing_or_falling_along_the_keys(mode, D, dtype, direction):
 
 
 @pytest.mark.parametrize("mode,D,dtype,bs", [("causal", 128, "bf16", 0), ("none", 64, "f16", 0),
+                                             ("causal", 16, "bf16", 0), ("none", 32, "f16", 0),
                                              ("block_diag", 128, "f16", 128),
                                              ("causal", 256, "bf16_v_e5m2", 0)])
 def test_deterministic(mode, D, dtype, bs):

@@ -85,6 +85,7 @@ struct Params {
   int bh;          // batch * heads
   int n_qblocks;   // query blocks per (batch, head)
   int group;       // causal: heads per longest-first group within an XCD (see block_coords)
+  int tail;        // causal: the shortest query blocks, run by every XCD after all longer ones
   float c;         // sm_scale * log2(e)
 };
 
@@ -226,14 +227,24 @@ __device__ __forceinline__ int swz_v(int r) {
 // blocks differ in length (block qb walks qb + 1 key blocks), so an XCD runs its heads in groups
 // of `group`, all query blocks of a group longest first: the blocks that start last are short
 // and the XCD's CUs finish together.  The host sizes the group so that its K/V fits the L2.
+// With `tail` > 0 the `tail` shortest blocks of every head are held back and run after all other
+// blocks of the XCD, longest first across its heads: otherwise the last group's longest blocks
+// start late and leave CUs idle at the end.
 __device__ __forceinline__ void block_coords(int id, int total, int nqb, bool heavy_first, int group,
-                                             int& bh, int& qb) {
+                                             int tail, int& bh, int& qb) {
   const int per_xcd = total >> 3;
-  if ((total & 7) == 0 && heavy_first && per_xcd % (nqb * group) == 0) {
+  if ((total & 7) == 0 && heavy_first && per_xcd % (nqb * group) == 0 && tail < nqb) {
     const int x = id & 7, j = id >> 3;
-    const int g = j / (group * nqb), r = j - g * (group * nqb);
-    qb = nqb - 1 - r / group;
-    bh = x * (per_xcd / nqb) + g * group + r % group;
+    const int hx = per_xcd / nqb, nl = nqb - tail;   // heads of this XCD, blocks run in groups
+    if (j < hx * nl) {
+      const int g = j / (group * nl), r = j - g * (group * nl);
+      qb = nqb - 1 - r / group;
+      bh = x * hx + g * group + r % group;
+    } else {
+      const int j2 = j - hx * nl;
+      qb = tail - 1 - j2 / hx;
+      bh = x * hx + j2 % hx;
+    }
     return;
   }
   int logical = id;
@@ -306,7 +317,7 @@ void attn_fwd_kernel(Params p) {
   const int col = lane & 31;      // the lane's query within the wave's 32
 
   int bh, qb;
-  block_coords(blockIdx.x, gridDim.x, p.n_qblocks, MODE == kMaskCausal, p.group, bh, qb);
+  block_coords(blockIdx.x, gridDim.x, p.n_qblocks, MODE == kMaskCausal, p.group, p.tail, bh, qb);
   const int L = p.L;
   const int m0 = qb * C::BM;              // first query row of the workgroup
   const int qw0 = m0 + 32 * wave;         // first query row of this wave
@@ -1004,6 +1015,7 @@ hipError_t launch(const Params& p0, hipStream_t stream) {
   const long long blocks = (long long)p.n_qblocks * p.bh;
   // causal head groups: the largest divisor of the heads per XCD whose K/V fits the 4 MiB L2
   p.group = 1;
+  p.tail = 0;   // (measured: no gain here at head dims 128 and 256)
   if (MODE == kMaskCausal && p.bh % 8 == 0) {
     const long long head_kv = (long long)p.L * D * (2 + C::VB);
     const int hx = p.bh / 8;

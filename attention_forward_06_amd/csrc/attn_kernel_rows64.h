@@ -53,7 +53,7 @@ void attn_fwd_rows64_kernel(Params p) {
   const int col = lane & 31;
 
   int bh, qb;
-  block_coords(blockIdx.x, gridDim.x, p.n_qblocks, MODE == kMaskCausal, p.group, bh, qb);
+  block_coords(blockIdx.x, gridDim.x, p.n_qblocks, MODE == kMaskCausal, p.group, p.tail, bh, qb);
   const int L = p.L;
   const int m0 = qb * BM;
   const int qw0 = m0 + 64 * wave;   // the wave's rows: [qw0, qw0 + 64)
@@ -446,8 +446,10 @@ hipError_t launch_rows64(const Params& p0, hipStream_t stream) {
   Params p = p0;
   p.n_qblocks = (p.L + BM - 1) / BM;
   const long long blocks = (long long)p.n_qblocks * p.bh;
-  // causal head groups: the largest divisor of the heads per XCD whose K/V fits the 4 MiB L2
+  // causal head groups: the largest divisor of the heads per XCD whose K/V fits the 4 MiB L2;
+  // the shortest quarter of every head's query blocks runs after all the others (block_coords)
   p.group = 1;
+  p.tail = p.n_qblocks / 4;
   if (MODE == kMaskCausal && p.bh % 8 == 0) {
     const long long head_kv = (long long)p.L * D * 4;
     const int hx = p.bh / 8;

@@ -331,6 +331,9 @@ def test_lse_output(mode, D, dtype, bs, L):
     (3, 4, 96, 64, "bf16", "block_diag", 32),
     (2, 8, 777, 16, "f16", "causal", 0),
     (2, 8, 640, 32, "bf16", "none", 0),
+    # causal head dims <= 64: several head groups per XCD, then each head's shortest blocks
+    (4, 32, 4096, 64, "f16", "causal", 0),
+    (2, 16, 1536, 32, "bf16", "causal", 0),
     # large grids: 8192 workgroups each (64-head causal groups per XCD)
     (64, 128, 256, 64, "f16", "causal", 0),
     (16, 64, 1000, 32, "f16", "none", 0),

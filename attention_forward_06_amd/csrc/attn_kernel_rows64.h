@@ -171,7 +171,7 @@ void attn_fwd_rows64_kernel(Params p) {
   };
 
   // General iteration: any mask, exact row max with the capped rescale, one row group after the
-  // other (compiler-scheduled; it runs on the first tile, the causal diagonal and a ragged tail).
+  // other (compiler-scheduled; it runs on the causal diagonal and a ragged tail).
   auto general = [&](int t, const unsigned char* kb, const unsigned char* vb, unsigned char* kb_dma,
                      unsigned char* vb_dma) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA of tile t landed

@@ -116,7 +116,8 @@ def test_workload_full_size(name):
     assert worst <= TOL[dt]
 
 
-@pytest.mark.parametrize("mode,D,dtype", [("causal", 128, "bf16"), ("none", 64, "f16")])
+@pytest.mark.parametrize("mode,D,dtype", [("causal", 128, "bf16"), ("none", 64, "f16"), ("causal", 64, "bf16"),
+                                          ("causal", 32, "f16")])
 def test_long_sequence_sampled_rows(mode, D, dtype):
     # L = 65536: the longest key loop and the largest in-head offsets among the tests
     B, H, L = 1, 2, 65536
